@@ -1,0 +1,117 @@
+"""Pins for stochastic rounding and its counter-based random source:
+the page's SR mini-example, exact enumeration of the probability, the
+unbiasedness statistic, Philox known-answer vectors and uniformity."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from tests import bruteforce as BF
+from tests.test_oracle_quantize import _toy
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _kat():
+    rows = []
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                v = [int(t, 16) for t in line.split()]
+                rows.append((v[0:4], v[4:6], v[6:10]))
+    return rows
+
+
+@pytest.mark.parametrize("ctr,key,want", _kat())
+def test_philox_known_answers(ctr, key, want):
+    assert list(O.philox4x32_10(ctr, key)) == want
+    assert BF.philox(ctr, key) == want
+
+
+def test_sr_bits_layout():
+    # element e takes 16-bit half (e mod 8) of the call with counter e // 8
+    seed, stream = 0x123456789ABCDEF0, 5
+    for e in [0, 1, 7, 8, 15, 2**33 + 3]:
+        j = e // 8
+        out = O.philox4x32_10([j & 0xFFFFFFFF, j >> 32, stream, 0],
+                              [seed & 0xFFFFFFFF, seed >> 32])
+        w = out[(e % 8) // 2]
+        want = (w & 0xFFFF) if e % 2 == 0 else (w >> 16)
+        assert O.sr_bits(seed, stream, e) == want == BF.sr_bits(seed, stream, e)
+
+
+def _count_up(m):
+    r = np.arange(65536, dtype=np.uint32)
+    idx = O.e2m1_sr_index_n(np.full(65536, m, np.float32), r)
+    return idx
+
+
+@pytest.mark.parametrize("m", [0.1, 0.26, 0.5, 0.74, 1.03, 1.2499, 1.6, 2.2, 2.9999, 3.5, 4.7, 5.99])
+def test_sr_exact_enumeration(m):
+    """Over all 2^16 values of the 16-bit draw the round-up count equals
+    ceil(frac * 2^16) with frac = (m - lo)/(hi - lo) computed exactly."""
+    from fractions import Fraction
+    m32 = np.float32(m)
+    idx = _count_up(m32)
+    tv = BF.E2M1
+    mf = Fraction(float(m32))
+    lo = max(i for i, t in enumerate(tv) if t <= mf)
+    frac = (mf - tv[lo]) / (tv[lo + 1] - tv[lo])
+    n_up = int((idx == lo + 1).sum())
+    assert set(np.unique(idx)) <= {lo, lo + 1}
+    want = -((-frac * 65536).numerator // (frac * 65536).denominator)  # ceil
+    assert n_up == want
+
+
+def test_sr_page_mini_example():
+    """Page SR mini-example: 1.03 between 1 and 1.5 rounds to 1 with
+    probability 0.94 and to 1.5 with 0.06 (to the page's two digits), and the
+    expectation is 1.03."""
+    v, lo, hi, p_lo, p_hi = _toy()["sr"][0]
+    idx = _count_up(np.float32(v))
+    vals = np.array([O.e2m1_decode(int(i)) for i in idx])
+    assert set(np.unique(vals)) == {lo, hi}
+    f_hi = np.mean(vals == hi)
+    assert abs(f_hi - p_hi) < 0.005 and abs((1 - f_hi) - p_lo) < 0.005
+    assert abs(vals.mean() - v) < 2 ** -16
+
+
+def test_sr_saturation_and_grid_points():
+    for m in (6.0, 6.5, 1e9):
+        assert set(np.unique(_count_up(np.float32(m)))) == {7}
+    for i, t in enumerate([0, .5, 1, 1.5, 2, 3, 4]):
+        assert set(np.unique(_count_up(np.float32(t)))) == {i}  # exact grid values never move
+
+
+def test_sr_unbiased_over_seeded_draws():
+    """1e5 seeded draws per value through the counter-based stream: the mean
+    of the rounded values is within 5 sigma of the input."""
+    n = 100_000
+    for k, v in enumerate([0.13, 0.61, 1.03, 1.37, 2.71, 3.3, 4.9, 5.5]):
+        r = O.sr_bits_n(1234, 0, k * n, n)
+        idx = O.e2m1_sr_index_n(np.full(n, v, np.float32), r)
+        vals = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])[idx]
+        lo, hi = vals.min(), vals.max()
+        p = (v - lo) / (hi - lo) if hi > lo else 0.0
+        sigma = (hi - lo) * np.sqrt(p * (1 - p) / n) + 1e-12
+        assert abs(vals.mean() - v) < 5 * sigma, (v, vals.mean(), sigma)
+
+
+def test_sr_stream_is_uniform():
+    """Chi-square of 16-bit halves in 256 bins and of their low bytes."""
+    r = O.sr_bits_n(42, 0, 0, 1 << 20)
+    for vals, bins in ((r >> 8, 256), (r & 0xFF, 256)):
+        h = np.bincount(vals.astype(np.int64), minlength=bins)
+        exp = r.size / bins
+        chi2 = ((h - exp) ** 2 / exp).sum()
+        assert chi2 < bins - 1 + 6 * np.sqrt(2 * (bins - 1))
+    # different streams and seeds give different draws
+    assert not np.array_equal(O.sr_bits_n(42, 1, 0, 64), r[:64])
+    assert not np.array_equal(O.sr_bits_n(43, 0, 0, 64), r[:64])
+
+
+def test_rht_signs_from_seed():
+    assert O.rht_signs_from_seed(0) == O.philox4x32_10([0, 0, 0, 0], [0, 0])[0] & 0xFFFF
+    assert O.rht_signs_from_seed(0) == 0xE8D5  # low half of the first KAT word
