@@ -1,0 +1,195 @@
+"""Benchmark: NVFP4 linear layer forward + backward on one MI355X.
+
+One step = the whole hot path of one training step of the layer
+Y = X W^T (X [8192, 5120], W [20480, 5120], dY [8192, 20480], bf16 inputs
+resident in HBM): quantise X (row copy + RHT'd column copy), W (16x16 scales +
+transposed copy) and dY (stochastic row copy + RHT'd stochastic column copy),
+then the Fprop, Dgrad and Wgrad GEMMs.  The timed step calls the C ABI entry
+points nvfp4_linear_fwd and nvfp4_linear_bwd.
+
+value = 3 * 2 * M * N * K / step time  (TFLOP/s, whole job, one GPU).
+A second timed pass issues the same kernels through the per-operation entry
+points with HIP events between them on the launch stream, giving the
+per-phase times behind `quantize_GBps` and the GEMM roofline.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 linear fwd+bwd TFLOP/s + quantize GB/s (8192 tok, 5120→20480)"
+M, K, N = 8192, 5120, 20480
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBPS = 8000.0
+
+# Algorithmic bytes of the quantisers, per source element (bf16 input):
+# read 2 B; each copy writes 0.5 B of codes + 1/16 B of 1x16 scales, or
+# 1/256 B of 16x16 scales.
+BYTES_ROWCOL = 2.0 + 2 * (0.5 + 1.0 / 16)
+BYTES_2D = 2.0 + 2 * (0.5 + 1.0 / 256)
+
+# HBM traffic of the GEMM kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# (scaled by a copy kernel's reading), valid only for the kernel source it
+# was measured on.
+GEMM_TRAFFIC = {"source_sha1": None, "bytes_per_launch": None}
+
+
+def _gemm_source_sha1() -> str:
+    with open(os.path.join(ROOT, "bit_quantized_numerics_amd", "csrc", "gemm.hip"), "rb") as f:
+        return hashlib.sha1(f.read()).hexdigest()
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    return p.parse_args()
+
+
+def cpu_baseline(sample_tokens: int):
+    """The oracle, as it stands, on a bounded sample of the same step: the
+    layer with `sample_tokens` tokens (W stays full size)."""
+    import numpy as np
+
+    import oracle as O
+    import workloads as W
+    Ms = sample_tokens
+    x = W.activations(Ms, K).float().numpy()
+    w = W.weights(N, K).float().numpy()
+    dy = W.gradients(Ms, N).float().numpy()
+    signs = O.rht_signs_from_seed(W.RHT_SEED)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    ops = O.linear_operands(x, w, dy, O.Recipe(rht_signs=signs, sr_seed=W.SR_SEED))
+    t1 = time.perf_counter()
+    for a, b in (("xq", "wq"), ("dyq", "wqt"), ("dyqt", "xqt")):
+        O.gemm(ops[a], ops[b])
+    t2 = time.perf_counter()
+    flops = 3 * 2.0 * Ms * N * K
+    qbytes = BYTES_ROWCOL * (Ms * K + Ms * N) + BYTES_2D * N * K
+    _ = np
+    return {
+        "value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"one layer step at {Ms} tokens (K={K}, N={N}, W full size): all six "
+                  f"quantisations + three float64 GEMMs; {t2 - t0:.2f} s",
+        "quantize_GBps": qbytes / (t1 - t0) / 1e9,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_numerics_amd as nv
+    import workloads as W
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    x = W.activations(M, K).to(dev)
+    w = W.weights(N, K).to(dev)
+    dy = W.gradients(M, N).to(dev)
+    signs = nv.nvfp4_rht_signs_from_seed(W.RHT_SEED)
+    ws = nv.Workspace(dev)
+    nv.nvfp4_workspace_init(ws)
+    ctx = nv.LinearContext(M, K, N, dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(N, K, dtype=torch.float32, device=dev)
+
+    def step():
+        nv.nvfp4_linear_fwd(x, w, ctx, ws, signs, training=True, y=y)
+        nv.nvfp4_linear_bwd(dy, ctx, ws, signs, W.SR_SEED, dx=dx, dw=dw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert nv.nvfp4_device_status(ws) == nv.OK
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+    flops = 3 * 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    # ---- per-phase breakdown: the same kernels through the per-op entry points
+    stream = torch.cuda.current_stream()
+    names = ["quant_x", "quant_w", "gemm_fprop", "quant_dy", "gemm_dgrad", "gemm_wgrad"]
+
+    def phases():
+        yield lambda: nv.nvfp4_quantize_rowcol(x, ws, ctx.xq, ctx.xqt, rht=True, rht_signs=signs)
+        yield lambda: nv.nvfp4_quantize_2d(w, ws, ctx.wq, ctx.wqt)
+        yield lambda: nv.nvfp4_gemm(ctx.xq, ctx.wq, c=y)
+        yield lambda: nv.nvfp4_quantize_rowcol(dy, ws, ctx.dyq, ctx.dyqt, round_row=nv.SR,
+                                               round_col=nv.SR, rht=True, rht_signs=signs,
+                                               seed=W.SR_SEED)
+        yield lambda: nv.nvfp4_gemm(ctx.dyq, ctx.wqt, c=dx)
+        yield lambda: nv.nvfp4_gemm(ctx.dyqt, ctx.xqt, c=dw)
+
+    for _ in range(2):
+        for f in phases():
+            f()
+    torch.cuda.synchronize()
+    reps = max(3, args.steps // 2)
+    tot = {n: 0.0 for n in names}
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        ev[0].record(stream)
+        for i, f in enumerate(phases()):
+            f()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            tot[n] += ev[i].elapsed_time(ev[i + 1])
+    ph = {n: tot[n] / reps for n in names}  # ms
+    gemm_ms = (ph["gemm_fprop"] + ph["gemm_dgrad"] + ph["gemm_wgrad"]) / 3
+    quant_ms = ph["quant_x"] + ph["quant_w"] + ph["quant_dy"]
+    qbytes = BYTES_ROWCOL * (M * K + M * N) + BYTES_2D * N * K
+    gemm_flops = 2.0 * M * N * K
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    traffic = None
+    if GEMM_TRAFFIC["source_sha1"] == _gemm_source_sha1():
+        traffic = GEMM_TRAFFIC["bytes_per_launch"]
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "NVFP4 linear layer fwd+bwd (Fprop+Dgrad+Wgrad, all quantisations), "
+                               "8192 tokens, 5120->20480",
+                   "M": M, "K": K, "N": N, "input_dtype": "bf16", "y_dx_dtype": "bf16",
+                   "dw_dtype": "f32", "recipe": "2D W scales, RHT16 on Wgrad inputs, SR on dY"},
+        "quantize_GBps": round(qbytes / (quant_ms * 1e-3) / 1e9, 1),
+        "quantize_frac_of_hbm_peak": round(qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "phase_ms": {n: round(v, 4) for n, v in ph.items()},
+        "roofline": {"bound": "mfma", "kernel": "nvfp4 gemm (f16 MFMA, fp32 acc), avg of 3 launches",
+                     "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

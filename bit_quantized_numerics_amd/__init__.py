@@ -1,0 +1,311 @@
+"""Python binding of libnvfp4.so, the MI355X (gfx950) NVFP4 linear-layer library.
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI of ``include/nvfp4.h``.  PyTorch supplies device memory and
+the current HIP stream.  There is no fallback: if the built library is
+missing, importing this package raises.
+
+Functions carry the C names (``nvfp4_quantize`` ...) and take torch tensors;
+``NVFP4Tensor`` owns the device buffers of one quantised operand and
+``Workspace`` the small status/reduction buffer every call needs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -m bit_quantized_numerics_amd.build "
+        "or __graft_entry__.build()); there is no non-HIP fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ------------------------------------------------------------------ C types
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_HIP, ERR_NONFINITE = range(8)
+F32, BF16 = 0, 1
+RN, SR = 0, 1
+SCALE_1X16, SCALE_16X16 = 0, 1
+
+
+class c_tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("scale_mode", ctypes.c_int32)]
+
+
+class c_quant_opts(ctypes.Structure):
+    _fields_ = [("round", ctypes.c_int32), ("transpose", ctypes.c_int32), ("rht", ctypes.c_int32),
+                ("rht_signs", ctypes.c_uint32), ("seed", ctypes.c_uint64),
+                ("offset", ctypes.c_uint64), ("stream_id", ctypes.c_uint32)]
+
+
+class c_recipe(ctypes.Structure):
+    _fields_ = [("rht_signs", ctypes.c_uint32), ("training", ctypes.c_int32)]
+
+
+class c_linear_ctx(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("xq", c_tensor), ("wq", c_tensor), ("wqt", c_tensor), ("xqt", c_tensor),
+                ("dyq", c_tensor), ("dyqt", c_tensor)]
+
+
+_vp, _i64, _i32, _u32, _u64, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t)
+_T = ctypes.POINTER(c_tensor)
+_SIGS = {
+    "nvfp4_tensor_bytes": (_i32, [_i64, _i64, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "nvfp4_workspace_bytes": (_sz, []),
+    "nvfp4_rht_signs_from_seed": (_u32, [_u64]),
+    "nvfp4_workspace_init": (_i32, [_vp, _sz, _vp]),
+    "nvfp4_device_status": (_i32, [_vp, _vp]),
+    "nvfp4_status_string": (ctypes.c_char_p, [_i32]),
+    "nvfp4_quantize": (_i32, [_vp, _i32, _i64, _i64, _i64, ctypes.POINTER(c_quant_opts), _T, _vp,
+                              _sz, _vp]),
+    "nvfp4_quantize_rowcol": (_i32, [_vp, _i32, _i64, _i64, _i64, ctypes.POINTER(c_quant_opts),
+                                     ctypes.POINTER(c_quant_opts), _T, _T, _vp, _sz, _vp]),
+    "nvfp4_quantize_2d": (_i32, [_vp, _i32, _i64, _i64, _i64, _T, _T, _vp, _sz, _vp]),
+    "nvfp4_rht16": (_i32, [_vp, _vp, _i32, _i64, _i64, _i64, _i32, _u32, _vp]),
+    "nvfp4_gemm": (_i32, [_T, _T, _vp, _i32, _i64, _vp, _sz, _vp]),
+    "nvfp4_linear_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.POINTER(c_recipe),
+                                ctypes.POINTER(c_linear_ctx), _vp, _sz, _vp]),
+    "nvfp4_linear_bwd": (_i32, [_vp, _i32, ctypes.POINTER(c_linear_ctx), _vp, _vp, _i32, _u64,
+                                ctypes.POINTER(c_recipe), _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.nvfp4_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise NVFP4Error(status, where)
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise NVFP4Error(ERR_DTYPE, f"dtype {t.dtype}")
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise NVFP4Error(ERR_SHAPE, "expected a 2D tensor with unit column stride")
+    return t.stride(0)
+
+
+# ------------------------------------------------------------------ buffers
+class Workspace:
+    """Device status word + reduction slots (nvfp4_workspace_bytes() bytes)."""
+
+    def __init__(self, device="cuda"):
+        self.nbytes = int(_lib.nvfp4_workspace_bytes())
+        self.buf = torch.zeros(self.nbytes, dtype=torch.uint8, device=device)
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.buf.data_ptr())
+
+
+class NVFP4Tensor:
+    """Device buffers of one quantised operand [rows, cols] (cols = block axis)."""
+
+    def __init__(self, rows: int, cols: int, scale_mode: int = SCALE_1X16, device="cuda"):
+        cb, sb = _sz(0), _sz(0)
+        _check(_lib.nvfp4_tensor_bytes(rows, cols, scale_mode, ctypes.byref(cb), ctypes.byref(sb)),
+               "nvfp4_tensor_bytes")
+        self.rows, self.cols, self.scale_mode = rows, cols, scale_mode
+        self.codes = torch.empty(cb.value, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(sb.value, dtype=torch.uint8, device=device)
+        self.global_scale = torch.empty(1, dtype=torch.float32, device=device)
+
+    def c(self) -> c_tensor:
+        return c_tensor(self.codes.data_ptr(), self.scales.data_ptr(), self.global_scale.data_ptr(),
+                        self.rows, self.cols, self.scale_mode)
+
+    def update(self, ct: c_tensor):
+        self.rows, self.cols, self.scale_mode = ct.rows, ct.cols, ct.scale_mode
+
+    def codes_2d(self):
+        return self.codes.view(self.rows, self.cols // 2)
+
+    def scales_2d(self):
+        if self.scale_mode == SCALE_1X16:
+            return self.scales.view(self.rows, self.cols // 16)
+        return self.scales.view(self.rows // 16, self.cols // 16)
+
+
+# ------------------------------------------------------------------ calls
+def nvfp4_tensor_bytes(rows: int, cols: int, scale_mode: int = SCALE_1X16):
+    cb, sb = _sz(0), _sz(0)
+    _check(_lib.nvfp4_tensor_bytes(rows, cols, scale_mode, ctypes.byref(cb), ctypes.byref(sb)),
+           "nvfp4_tensor_bytes")
+    return cb.value, sb.value
+
+
+def nvfp4_workspace_bytes() -> int:
+    return int(_lib.nvfp4_workspace_bytes())
+
+
+def nvfp4_rht_signs_from_seed(seed: int) -> int:
+    return int(_lib.nvfp4_rht_signs_from_seed(seed))
+
+
+def nvfp4_status_string(status: int) -> str:
+    return _lib.nvfp4_status_string(status).decode()
+
+
+def nvfp4_workspace_init(ws: Workspace):
+    _check(_lib.nvfp4_workspace_init(ws.ptr, ws.nbytes, _stream(ws.buf.device)), "nvfp4_workspace_init")
+
+
+def nvfp4_device_status(ws: Workspace) -> int:
+    return int(_lib.nvfp4_device_status(ws.ptr, _stream(ws.buf.device)))
+
+
+def _opts(round_mode=RN, transpose=False, rht=False, rht_signs=0, seed=0, offset=0, stream_id=0):
+    return c_quant_opts(int(round_mode), int(transpose), int(rht), int(rht_signs), int(seed),
+                        int(offset), int(stream_id))
+
+
+def nvfp4_quantize(x: torch.Tensor, ws: Workspace, out: NVFP4Tensor | None = None, *,
+                   round_mode=RN, transpose=False, rht=False, rht_signs=0, seed=0, offset=0,
+                   stream_id=0) -> NVFP4Tensor:
+    rows, cols = x.shape
+    if out is None:
+        out = (NVFP4Tensor(cols, rows, device=x.device) if transpose
+               else NVFP4Tensor(rows, cols, device=x.device))
+    o = _opts(round_mode, transpose, rht, rht_signs, seed, offset, stream_id)
+    ct = out.c()
+    _check(_lib.nvfp4_quantize(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), rows, cols, _ld(x),
+                               ctypes.byref(o), ctypes.byref(ct), ws.ptr, ws.nbytes,
+                               _stream(x.device)), "nvfp4_quantize")
+    out.update(ct)
+    return out
+
+
+def nvfp4_quantize_rowcol(x: torch.Tensor, ws: Workspace, row: NVFP4Tensor | None = None,
+                          col: NVFP4Tensor | None = None, *, round_row=RN, round_col=RN,
+                          rht=True, rht_signs=0, seed=0, offset_row=0, offset_col=0,
+                          stream_row=0, stream_col=1):
+    rows, cols = x.shape
+    row = row or NVFP4Tensor(rows, cols, device=x.device)
+    col = col or NVFP4Tensor(cols, rows, device=x.device)
+    o_r = _opts(round_row, False, False, rht_signs, seed, offset_row, stream_row)
+    o_c = _opts(round_col, True, rht, rht_signs, seed, offset_col, stream_col)
+    cr, cc = row.c(), col.c()
+    _check(_lib.nvfp4_quantize_rowcol(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), rows, cols,
+                                      _ld(x), ctypes.byref(o_r), ctypes.byref(o_c),
+                                      ctypes.byref(cr), ctypes.byref(cc), ws.ptr, ws.nbytes,
+                                      _stream(x.device)), "nvfp4_quantize_rowcol")
+    row.update(cr)
+    col.update(cc)
+    return row, col
+
+
+def nvfp4_quantize_2d(w: torch.Tensor, ws: Workspace, out: NVFP4Tensor | None = None,
+                      out_t: NVFP4Tensor | None = None, want_t: bool = True):
+    rows, cols = w.shape
+    out = out or NVFP4Tensor(rows, cols, SCALE_16X16, device=w.device)
+    if want_t and out_t is None:
+        out_t = NVFP4Tensor(cols, rows, SCALE_16X16, device=w.device)
+    co = out.c()
+    ct = out_t.c() if out_t is not None else None
+    _check(_lib.nvfp4_quantize_2d(ctypes.c_void_p(w.data_ptr()), _dtype_code(w), rows, cols, _ld(w),
+                                  ctypes.byref(co), ctypes.byref(ct) if ct is not None else None,
+                                  ws.ptr, ws.nbytes, _stream(w.device)), "nvfp4_quantize_2d")
+    out.update(co)
+    if out_t is not None:
+        out_t.update(ct)
+    return out, out_t
+
+
+def nvfp4_rht16(x: torch.Tensor, axis: int, rht_signs: int, y: torch.Tensor | None = None):
+    rows, cols = x.shape
+    y = y if y is not None else torch.empty(rows, cols, dtype=torch.float32, device=x.device)
+    _check(_lib.nvfp4_rht16(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                            _dtype_code(x), rows, cols, _ld(x), axis, rht_signs, _stream(x.device)),
+           "nvfp4_rht16")
+    return y
+
+
+def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, c: torch.Tensor | None = None,
+               ws: Workspace | None = None):
+    if c is None:
+        c = torch.empty(a.rows, b.rows, dtype=out_dtype, device=a.codes.device)
+    ca, cb = a.c(), b.c()
+    _check(_lib.nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), ctypes.c_void_p(c.data_ptr()),
+                           _dtype_code(c), _ld(c), ws.ptr if ws else None, ws.nbytes if ws else 0,
+                           _stream(c.device)), "nvfp4_gemm")
+    return c
+
+
+class LinearContext:
+    """Caller-owned quantised operands of one layer step (Y = X W^T)."""
+
+    def __init__(self, M: int, K: int, N: int, device="cuda"):
+        self.M, self.K, self.N = M, K, N
+        self.xq = NVFP4Tensor(M, K, device=device)
+        self.wq = NVFP4Tensor(N, K, SCALE_16X16, device=device)
+        self.wqt = NVFP4Tensor(K, N, SCALE_16X16, device=device)
+        self.xqt = NVFP4Tensor(K, M, device=device)
+        self.dyq = NVFP4Tensor(M, N, device=device)
+        self.dyqt = NVFP4Tensor(N, M, device=device)
+        self.cctx = c_linear_ctx(M, K, N, self.xq.c(), self.wq.c(), self.wqt.c(), self.xqt.c(),
+                                 self.dyq.c(), self.dyqt.c())
+
+    def sync_shapes(self):
+        for name in ("xq", "wq", "wqt", "xqt", "dyq", "dyqt"):
+            getattr(self, name).update(getattr(self.cctx, name))
+
+
+def nvfp4_linear_fwd(x: torch.Tensor, w: torch.Tensor, ctx: LinearContext, ws: Workspace,
+                     rht_signs: int, training: bool = True, y: torch.Tensor | None = None):
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    rec = c_recipe(rht_signs, int(training))
+    _check(_lib.nvfp4_linear_fwd(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                                 ctypes.c_void_p(y.data_ptr()), M, K, N, _dtype_code(x),
+                                 ctypes.byref(rec), ctypes.byref(ctx.cctx), ws.ptr, ws.nbytes,
+                                 _stream(x.device)), "nvfp4_linear_fwd")
+    ctx.sync_shapes()
+    return y
+
+
+def nvfp4_linear_bwd(dy: torch.Tensor, ctx: LinearContext, ws: Workspace, rht_signs: int,
+                     sr_seed: int, dw_dtype=torch.float32, dx: torch.Tensor | None = None,
+                     dw: torch.Tensor | None = None):
+    if dx is None:
+        dx = torch.empty(ctx.M, ctx.K, dtype=torch.bfloat16, device=dy.device)
+    if dw is None:
+        dw = torch.empty(ctx.N, ctx.K, dtype=dw_dtype, device=dy.device)
+    rec = c_recipe(rht_signs, 1)
+    _check(_lib.nvfp4_linear_bwd(ctypes.c_void_p(dy.data_ptr()), _dtype_code(dy), ctypes.byref(ctx.cctx),
+                                 ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(dw.data_ptr()),
+                                 _dtype_code(dw), sr_seed, ctypes.byref(rec), ws.ptr, ws.nbytes,
+                                 _stream(dy.device)), "nvfp4_linear_bwd")
+    ctx.sync_shapes()
+    return dx, dw

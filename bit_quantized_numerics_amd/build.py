@@ -1,0 +1,48 @@
+"""Compile the HIP sources into libnvfp4.so (gfx950) next to this file.
+
+Flags that the numerics depend on:
+  -ffp-contract=off                         no FMA contraction: every fp32 step rounds once
+  -fno-gpu-flush-denormals-to-zero          IEEE denormals
+  -fhip-fp32-correctly-rounded-divide-sqrt  correctly rounded fp32 division
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                                            no packed-fp32 VALU instructions
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libnvfp4.so")
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles; returns the library path."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libnvfp4.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

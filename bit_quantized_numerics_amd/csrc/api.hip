@@ -1,0 +1,436 @@
+// api.hip -- the C ABI declared in include/nvfp4.h: argument validation,
+// workspace slots and kernel orchestration.  Every argument check happens
+// before anything is enqueued.
+//
+// Citations: [Review] = web page "NVFP4 4-bit Pretraining, Made Practical: 12B
+// up to 10T Tokens, Effectively On Par with FP8" (review of arXiv 2509.25149),
+// by numbered section; [Captions] = that paper's figure-caption list.
+#include "nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace {
+
+using namespace nvfp4;
+
+// Workspace: 64 uint32 words.  Word 0 is the sticky device status; the others
+// are amax slots (bit patterns of non-negative floats, reduced with atomicMax).
+constexpr size_t kWorkspaceBytes = 256;
+constexpr int kWsWords = (int)(kWorkspaceBytes / 4);
+enum Slot {
+  kSlotStatus = 0,
+  kSlotQRaw = 1,   // nvfp4_quantize / rowcol / 2d: plain amax
+  kSlotQRht = 2,   //   ... amax after the RHT
+  kSlotXRaw = 3,   // layer forward: X
+  kSlotXRht = 4,   //   (R X)
+  kSlotW = 5,      //   W
+  kSlotDyRaw = 6,  // layer backward: dY
+  kSlotDyRht = 7,  //   (R dY)
+};
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+inline uint32_t* ws_word(void* ws, int slot) { return static_cast<uint32_t*>(ws) + slot; }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t elem_bytes(int dtype) { return dtype == NVFP4_BF16 ? 2 : 4; }
+
+nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+nvfp4_status check_workspace(void* ws, size_t bytes) {
+  if (!ws || bytes < kWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(ws, 4)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status check_source(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld) {
+  if (!x) return NVFP4_ERR_NULL;
+  if (dtype != NVFP4_F32 && dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows > (int64_t)65535 * 256) return NVFP4_ERR_SHAPE;  // grid y limit
+  if (ld < cols) return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || (ld * (int64_t)elem_bytes(dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status check_out(const nvfp4_tensor* t) {
+  if (!t || !t->codes || !t->scales || !t->global_scale) return NVFP4_ERR_NULL;
+  if (!aligned(t->codes, 16) || !aligned(t->global_scale, 4)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status check_opts(const nvfp4_quant_opts* o) {
+  if (!o) return NVFP4_ERR_NULL;
+  if (o->round != NVFP4_RN && o->round != NVFP4_SR) return NVFP4_ERR_DTYPE;
+  if (o->transpose != 0 && o->transpose != 1) return NVFP4_ERR_DTYPE;
+  if (o->rht != 0 && o->rht != 1) return NVFP4_ERR_DTYPE;
+  if (o->rht_signs > 0xFFFFu) return NVFP4_ERR_DTYPE;
+  if (o->offset % 16 != 0) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+CopyArgs copy_args(const nvfp4_tensor* t, void* ws, int slot, const nvfp4_quant_opts* o) {
+  CopyArgs c;
+  c.codes = t->codes;
+  c.scales = t->scales;
+  c.global = t->global_scale;
+  c.amax = ws_word(ws, slot);
+  if (o) {
+    c.seed = o->seed;
+    c.offset = o->offset;
+    c.stream = o->stream_id;
+  }
+  return c;
+}
+
+#define NVFP4_TRY(expr)                 \
+  do {                                  \
+    const nvfp4_status st_ = (expr);    \
+    if (st_ != NVFP4_OK) return st_;    \
+  } while (0)
+#define NVFP4_HIP(expr)                              \
+  do {                                               \
+    if ((expr) != hipSuccess) return NVFP4_ERR_HIP;  \
+  } while (0)
+
+// Philox4x32-10 on the host (for the RHT sign diagonal).
+void philox_host(uint32_t c[4], uint32_t k0, uint32_t k1) {
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    c[1] = (uint32_t)p1;
+    c[3] = (uint32_t)p0;
+    c[0] = n0;
+    c[2] = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+nvfp4_status check_gemm_operand(const nvfp4_tensor* t) {
+  if (!t || !t->codes || !t->scales || !t->global_scale) return NVFP4_ERR_NULL;
+  if (t->rows <= 0 || t->cols <= 0 || t->cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (t->scale_mode != NVFP4_SCALE_1X16 && t->scale_mode != NVFP4_SCALE_16X16) return NVFP4_ERR_DTYPE;
+  if (t->scale_mode == NVFP4_SCALE_16X16 && t->rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned(t->codes, 16) || !aligned(t->global_scale, 4)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+GemmOperand gemm_operand(const nvfp4_tensor* t) {
+  GemmOperand g;
+  g.codes = t->codes;
+  g.scales = t->scales;
+  g.global = t->global_scale;
+  g.rows = t->rows;
+  g.scale_shift = t->scale_mode == NVFP4_SCALE_16X16 ? 4 : 0;
+  return g;
+}
+
+void set_shape(nvfp4_tensor* t, int64_t rows, int64_t cols, int32_t mode) {
+  t->rows = rows;
+  t->cols = cols;
+  t->scale_mode = mode;
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_tensor_bytes(int64_t rows, int64_t cols, int32_t scale_mode, size_t* codes_bytes,
+                                size_t* scales_bytes) {
+  if (!codes_bytes || !scales_bytes) return NVFP4_ERR_NULL;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (scale_mode == NVFP4_SCALE_1X16) {
+    *scales_bytes = (size_t)(rows * (cols / 16));
+  } else if (scale_mode == NVFP4_SCALE_16X16) {
+    if (rows % 16 != 0) return NVFP4_ERR_SHAPE;
+    *scales_bytes = (size_t)((rows / 16) * (cols / 16));
+  } else {
+    return NVFP4_ERR_DTYPE;
+  }
+  *codes_bytes = (size_t)(rows * (cols / 2));
+  return NVFP4_OK;
+}
+
+size_t nvfp4_workspace_bytes(void) { return kWorkspaceBytes; }
+
+uint32_t nvfp4_rht_signs_from_seed(uint64_t seed) {
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  philox_host(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return c[0] & 0xFFFFu;
+}
+
+nvfp4_status nvfp4_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  NVFP4_TRY(check_workspace(workspace, ws_bytes));
+  NVFP4_HIP(launch_zero_words(static_cast<uint32_t*>(workspace), kWsWords, as_stream(stream)));
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_device_status(void* workspace, void* stream) {
+  if (!workspace) return NVFP4_ERR_WORKSPACE;
+  uint32_t word = 0;
+  NVFP4_HIP(hipMemcpyAsync(&word, workspace, 4, hipMemcpyDeviceToHost, as_stream(stream)));
+  NVFP4_HIP(hipStreamSynchronize(as_stream(stream)));
+  NVFP4_HIP(launch_zero_words(static_cast<uint32_t*>(workspace), 1, as_stream(stream)));
+  return word == 0 ? NVFP4_OK : (nvfp4_status)word;
+}
+
+const char* nvfp4_status_string(nvfp4_status s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "null pointer";
+    case NVFP4_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer, leading dimension or offset";
+    case NVFP4_ERR_DTYPE: return "unsupported dtype or enum value";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_HIP: return "HIP launch or runtime error";
+    case NVFP4_ERR_NONFINITE: return "non-finite tensor amax";
+  }
+  return "unknown status";
+}
+
+nvfp4_status nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                            const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  NVFP4_TRY(check_source(x, dtype, rows, cols, ld));
+  NVFP4_TRY(check_opts(opts));
+  NVFP4_TRY(check_out(out));
+  NVFP4_TRY(check_workspace(workspace, ws_bytes));
+  // The RHT runs along the operand's block axis; the recipe applies it to the
+  // column-wise (token-axis) Wgrad copies only [Review s3], which is the
+  // supported placement.
+  if (opts->rht && !opts->transpose) return NVFP4_ERR_SHAPE;
+  if (opts->transpose && rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  const hipStream_t s = as_stream(stream);
+
+  TileArgs a;
+  a.x = x;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.signs = opts->rht_signs;
+  a.status = ws_word(workspace, kSlotStatus);
+  int flags = 0;
+  const int slot = opts->rht ? kSlotQRht : kSlotQRaw;
+  if (opts->transpose) {
+    set_shape(out, cols, rows, NVFP4_SCALE_1X16);
+    a.col = copy_args(out, workspace, slot, opts);
+    flags = kFCol | (opts->rht ? kFRht : 0) | (opts->round == NVFP4_SR ? kFSrCol : 0);
+  } else {
+    set_shape(out, rows, cols, NVFP4_SCALE_1X16);
+    a.row = copy_args(out, workspace, slot, opts);
+    flags = kFRow | (opts->round == NVFP4_SR ? kFSrRow : 0);
+  }
+  NVFP4_HIP(launch_zero_words(ws_word(workspace, kSlotQRaw), 2, s));
+  NVFP4_HIP(launch_amax(x, dtype, rows, cols, ld, opts->rht_signs,
+                        opts->rht ? nullptr : ws_word(workspace, kSlotQRaw),
+                        opts->rht ? ws_word(workspace, kSlotQRht) : nullptr, s));
+  NVFP4_HIP(launch_quant_tile(dtype, flags, a, s));
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_quantize_rowcol(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                   int64_t ld, const nvfp4_quant_opts* opts_row,
+                                   const nvfp4_quant_opts* opts_col, nvfp4_tensor* row,
+                                   nvfp4_tensor* col, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  NVFP4_TRY(check_source(x, dtype, rows, cols, ld));
+  NVFP4_TRY(check_opts(opts_row));
+  NVFP4_TRY(check_opts(opts_col));
+  NVFP4_TRY(check_out(row));
+  NVFP4_TRY(check_out(col));
+  NVFP4_TRY(check_workspace(workspace, ws_bytes));
+  if (opts_row->transpose != 0 || opts_row->rht != 0 || opts_col->transpose != 1)
+    return NVFP4_ERR_SHAPE;
+  if (rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  const hipStream_t s = as_stream(stream);
+  set_shape(row, rows, cols, NVFP4_SCALE_1X16);
+  set_shape(col, cols, rows, NVFP4_SCALE_1X16);
+  TileArgs a;
+  a.x = x;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.signs = opts_col->rht_signs;
+  a.status = ws_word(workspace, kSlotStatus);
+  a.row = copy_args(row, workspace, kSlotQRaw, opts_row);
+  a.col = copy_args(col, workspace, opts_col->rht ? kSlotQRht : kSlotQRaw, opts_col);
+  const int flags = kFRow | kFCol | (opts_col->rht ? kFRht : 0) |
+                    (opts_row->round == NVFP4_SR ? kFSrRow : 0) |
+                    (opts_col->round == NVFP4_SR ? kFSrCol : 0);
+  NVFP4_HIP(launch_zero_words(ws_word(workspace, kSlotQRaw), 2, s));
+  NVFP4_HIP(launch_amax(x, dtype, rows, cols, ld, opts_col->rht_signs, ws_word(workspace, kSlotQRaw),
+                        opts_col->rht ? ws_word(workspace, kSlotQRht) : nullptr, s));
+  NVFP4_HIP(launch_quant_tile(dtype, flags, a, s));
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_quantize_2d(const void* w, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                               nvfp4_tensor* out, nvfp4_tensor* out_t, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  NVFP4_TRY(check_source(w, dtype, rows, cols, ld));
+  NVFP4_TRY(check_out(out));
+  if (out_t) NVFP4_TRY(check_out(out_t));
+  NVFP4_TRY(check_workspace(workspace, ws_bytes));
+  if (rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  const hipStream_t s = as_stream(stream);
+  set_shape(out, rows, cols, NVFP4_SCALE_16X16);
+  TileArgs a;
+  a.x = w;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.status = ws_word(workspace, kSlotStatus);
+  a.row = copy_args(out, workspace, kSlotQRaw, nullptr);
+  int flags = kFRow | kF2D;
+  if (out_t) {
+    set_shape(out_t, cols, rows, NVFP4_SCALE_16X16);
+    a.col = copy_args(out_t, workspace, kSlotQRaw, nullptr);
+    flags |= kFCol;
+  }
+  NVFP4_HIP(launch_zero_words(ws_word(workspace, kSlotQRaw), 1, s));
+  NVFP4_HIP(launch_amax(w, dtype, rows, cols, ld, 0, ws_word(workspace, kSlotQRaw), nullptr, s));
+  NVFP4_HIP(launch_quant_tile(dtype, flags, a, s));
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_rht16(const void* x, float* y, int32_t in_dtype, int64_t rows, int64_t cols,
+                         int64_t ld, int32_t axis, uint32_t rht_signs, void* stream) {
+  if (!x || !y) return NVFP4_ERR_NULL;
+  if (in_dtype != NVFP4_F32 && in_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  if (axis != 0 && axis != 1) return NVFP4_ERR_DTYPE;
+  if (rht_signs > 0xFFFFu) return NVFP4_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || ld < cols) return NVFP4_ERR_SHAPE;
+  if (axis == 1 && cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (axis == 0 && (rows % 16 != 0 || cols % 8 != 0)) return NVFP4_ERR_SHAPE;
+  if (rows > (int64_t)65535 * 256) return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 16) || (ld * (int64_t)elem_bytes(in_dtype)) % 16 != 0)
+    return NVFP4_ERR_ALIGN;
+  NVFP4_HIP(launch_rht16(x, y, in_dtype, rows, cols, ld, axis, rht_signs, as_stream(stream)));
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int32_t c_dtype,
+                        int64_t ldc, void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  NVFP4_TRY(check_gemm_operand(a));
+  NVFP4_TRY(check_gemm_operand(b));
+  if (!c) return NVFP4_ERR_NULL;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  if (a->cols != b->cols) return NVFP4_ERR_SHAPE;
+  if (ldc < b->rows) return NVFP4_ERR_SHAPE;
+  if (a->rows > (int64_t)65535 * 128) return NVFP4_ERR_SHAPE;
+  if (!aligned(c, 4)) return NVFP4_ERR_ALIGN;
+  NVFP4_HIP(launch_gemm(gemm_operand(a), gemm_operand(b), a->cols, c, c_dtype, ldc, as_stream(stream)));
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, int64_t K, int64_t N,
+                              int32_t dtype, const nvfp4_recipe* recipe, nvfp4_linear_ctx* ctx,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (!recipe || !ctx || !y) return NVFP4_ERR_NULL;
+  if (M % 16 || K % 16 || N % 16) return NVFP4_ERR_SHAPE;
+  NVFP4_TRY(check_source(x, dtype, M, K, K));
+  NVFP4_TRY(check_source(w, dtype, N, K, K));
+  NVFP4_TRY(check_out(&ctx->xq));
+  NVFP4_TRY(check_out(&ctx->wq));
+  NVFP4_TRY(check_out(&ctx->wqt));
+  if (recipe->training) NVFP4_TRY(check_out(&ctx->xqt));
+  if (recipe->rht_signs > 0xFFFFu) return NVFP4_ERR_DTYPE;
+  NVFP4_TRY(check_workspace(workspace, ws_bytes));
+  if (!aligned(y, 4)) return NVFP4_ERR_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  ctx->M = M;
+  ctx->K = K;
+  ctx->N = N;
+  set_shape(&ctx->xq, M, K, NVFP4_SCALE_1X16);
+  set_shape(&ctx->wq, N, K, NVFP4_SCALE_16X16);
+  set_shape(&ctx->wqt, K, N, NVFP4_SCALE_16X16);
+  NVFP4_HIP(launch_zero_words(ws_word(workspace, kSlotXRaw), 3, s));
+
+  // X: row-wise copy for Fprop and, when training, (R X)^T for Wgrad.
+  TileArgs ax;
+  ax.x = x;
+  ax.rows = M;
+  ax.cols = K;
+  ax.ld = K;
+  ax.signs = recipe->rht_signs;
+  ax.status = ws_word(workspace, kSlotStatus);
+  ax.row = copy_args(&ctx->xq, workspace, kSlotXRaw, nullptr);
+  int fx = kFRow;
+  if (recipe->training) {
+    set_shape(&ctx->xqt, K, M, NVFP4_SCALE_1X16);
+    ax.col = copy_args(&ctx->xqt, workspace, kSlotXRht, nullptr);
+    fx |= kFCol | kFRht;
+  }
+  NVFP4_HIP(launch_amax(x, dtype, M, K, K, recipe->rht_signs, ws_word(workspace, kSlotXRaw),
+                        recipe->training ? ws_word(workspace, kSlotXRht) : nullptr, s));
+  NVFP4_HIP(launch_quant_tile(dtype, fx, ax, s));
+
+  // W: 16x16 scales, with the transposed copy for Dgrad.
+  TileArgs aw;
+  aw.x = w;
+  aw.rows = N;
+  aw.cols = K;
+  aw.ld = K;
+  aw.status = ws_word(workspace, kSlotStatus);
+  aw.row = copy_args(&ctx->wq, workspace, kSlotW, nullptr);
+  aw.col = copy_args(&ctx->wqt, workspace, kSlotW, nullptr);
+  NVFP4_HIP(launch_amax(w, dtype, N, K, K, 0, ws_word(workspace, kSlotW), nullptr, s));
+  NVFP4_HIP(launch_quant_tile(dtype, kFRow | kFCol | kF2D, aw, s));
+
+  // Fprop: Y = Q(X) Q(W)^T
+  NVFP4_HIP(launch_gemm(gemm_operand(&ctx->xq), gemm_operand(&ctx->wq), K, y, kDtypeBF16, N, s));
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* ctx, void* dx,
+                              void* dw, int32_t dw_dtype, uint64_t sr_seed,
+                              const nvfp4_recipe* recipe, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  if (!ctx || !dx || !dw || !recipe) return NVFP4_ERR_NULL;
+  const int64_t M = ctx->M, K = ctx->K, N = ctx->N;
+  if (M <= 0 || M % 16 || K % 16 || N % 16) return NVFP4_ERR_SHAPE;
+  if (ctx->xqt.rows != K || ctx->xqt.cols != M || ctx->wqt.rows != K || ctx->wqt.cols != N)
+    return NVFP4_ERR_SHAPE;  // forward with training on this ctx has not run
+  NVFP4_TRY(check_source(dy, dtype, M, N, N));
+  if (dw_dtype != NVFP4_F32 && dw_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  NVFP4_TRY(check_out(&ctx->dyq));
+  NVFP4_TRY(check_out(&ctx->dyqt));
+  NVFP4_TRY(check_gemm_operand(&ctx->wqt));
+  NVFP4_TRY(check_gemm_operand(&ctx->xqt));
+  if (recipe->rht_signs > 0xFFFFu) return NVFP4_ERR_DTYPE;
+  NVFP4_TRY(check_workspace(workspace, ws_bytes));
+  if (!aligned(dx, 4) || !aligned(dw, 4)) return NVFP4_ERR_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  set_shape(&ctx->dyq, M, N, NVFP4_SCALE_1X16);
+  set_shape(&ctx->dyqt, N, M, NVFP4_SCALE_1X16);
+  NVFP4_HIP(launch_zero_words(ws_word(workspace, kSlotDyRaw), 2, s));
+
+  // dY: SR row copy (stream 0) and SR (R dY)^T (stream 1) from one read.
+  TileArgs ad;
+  ad.x = dy;
+  ad.rows = M;
+  ad.cols = N;
+  ad.ld = N;
+  ad.signs = recipe->rht_signs;
+  ad.status = ws_word(workspace, kSlotStatus);
+  nvfp4_quant_opts o_row{NVFP4_SR, 0, 0, recipe->rht_signs, sr_seed, 0, 0};
+  nvfp4_quant_opts o_col{NVFP4_SR, 1, 1, recipe->rht_signs, sr_seed, 0, 1};
+  ad.row = copy_args(&ctx->dyq, workspace, kSlotDyRaw, &o_row);
+  ad.col = copy_args(&ctx->dyqt, workspace, kSlotDyRht, &o_col);
+  NVFP4_HIP(launch_amax(dy, dtype, M, N, N, recipe->rht_signs, ws_word(workspace, kSlotDyRaw),
+                        ws_word(workspace, kSlotDyRht), s));
+  NVFP4_HIP(launch_quant_tile(dtype, kFRow | kFCol | kFRht | kFSrRow | kFSrCol, ad, s));
+
+  // Dgrad: dX = Q(dY) Q(W^T)^T [M, K];  Wgrad: dW = Q((R dY)^T) Q((R X)^T)^T [N, K]
+  NVFP4_HIP(launch_gemm(gemm_operand(&ctx->dyq), gemm_operand(&ctx->wqt), N, dx, kDtypeBF16, K, s));
+  NVFP4_HIP(launch_gemm(gemm_operand(&ctx->dyqt), gemm_operand(&ctx->xqt), M, dw,
+                        dw_dtype == NVFP4_BF16 ? kDtypeBF16 : kDtypeF32, K, s));
+  return NVFP4_OK;
+}
+
+}  // extern "C"

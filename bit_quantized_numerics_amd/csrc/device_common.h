@@ -1,0 +1,235 @@
+// device_common.h -- gfx950 device helpers shared by the NVFP4 kernels.
+//
+// Citations: [Review] = web page "NVFP4 4-bit Pretraining, Made Practical: 12B
+// up to 10T Tokens, Effectively On Par with FP8" (review of arXiv 2509.25149),
+// by numbered section; [Captions] = that paper's figure-caption list.
+//
+// Every fp32 step that decides a code is one IEEE operation rounded to nearest
+// even, in the order the C ABI header states (the library is built with
+// -ffp-contract=off, IEEE denormals and correctly rounded fp32 division), so
+// codes and scales are reproducible bit for bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Status word values (mirror nvfp4_status).
+constexpr uint32_t kStatusNonfinite = 7u;
+// Bit pattern of +inf: |x| bit patterns at or above it are Inf or NaN.
+constexpr uint32_t kInfBits = 0x7F800000u;
+
+// ---------------------------------------------------------------- loads
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight consecutive elements starting at p (16-byte aligned for bf16, 32 for fp32).
+__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+  v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+  v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// ---------------------------------------------------------------- cross-lane
+
+// Value of the neighbouring lane (lane ^ 1) via DPP quad_perm [1,0,3,2].
+__device__ __forceinline__ float lane_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- scales
+
+// Tensor scales from the amax bit pattern [Review s1 Step 1]:
+// s_enc = 2688/amax (saturated at FLT_MAX; 1 for amax 0), s6 = s_enc/6, g = 1/s_enc.
+struct TensorScales {
+  float s_enc, s6, g;
+};
+__device__ __forceinline__ TensorScales tensor_scales(uint32_t amax_bits) {
+  TensorScales ts;
+  const float amax = __uint_as_float(amax_bits);
+  if (amax == 0.0f) {
+    ts.s_enc = 1.0f;
+    ts.g = 1.0f;
+    ts.s6 = 1.0f / 6.0f;
+    return ts;
+  }
+  float s = 2688.0f / amax;
+  if (__builtin_isinf(s)) s = 3.402823466e38f;
+  ts.s_enc = s;
+  ts.g = 1.0f / s;
+  ts.s6 = s / 6.0f;
+  return ts;
+}
+
+// E4M3FN encode of a non-negative finite fp32, nearest-even, saturating at
+// 448 [Review s1 Step 2].  Returns the code; *val receives its value.
+__device__ __forceinline__ uint32_t e4m3_encode(float t, float* val) {
+  if (!(t >= 0x1p-6f)) {              // subnormal range, multiples of 2^-9
+    const float q = __builtin_rintf(t * 512.0f);  // 0..8, ties to even
+    *val = q * 0x1p-9f;
+    return (uint32_t)q;               // 8 is the code of 2^-6
+  }
+  if (t >= 448.0f) {
+    *val = 448.0f;
+    return 0x7Eu;
+  }
+  uint32_t b = __float_as_uint(t);
+  b += 0x7FFFFu + ((b >> 20) & 1u);   // round the mantissa to 3 bits, ties even
+  b &= 0xFFF00000u;
+  *val = __uint_as_float(b);
+  return (b >> 20) - 960u;            // rebias exponent 127 -> 7
+}
+
+// Element multiplier r_b = s_enc / d_b (0 for an all-zero block; saturated).
+__device__ __forceinline__ float elem_multiplier(float s_enc, float d) {
+  if (d == 0.0f) return 0.0f;
+  float r = s_enc / d;
+  if (__builtin_isinf(r)) r = 3.402823466e38f;
+  return r;
+}
+
+// Block scale and multiplier from a block amax.
+__device__ __forceinline__ float block_scale(float amax_b, const TensorScales& ts, uint32_t* code) {
+  float d;
+  *code = e4m3_encode(amax_b * ts.s6, &d);
+  return elem_multiplier(ts.s_enc, d);
+}
+
+// ---------------------------------------------------------------- E2M1 codes
+
+// Two fp32 values -> two E2M1 codes (nearest-even, saturating, sign of zero
+// kept) written into byte SEL of `old`; low nibble = a.  gfx950's convert
+// with unit scale performs exactly this rounding.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_rn(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Eight values -> eight nearest-even codes in one dword (value i in nibble i).
+__device__ __forceinline__ uint32_t fp4x8_rn(const float* v) {
+  uint32_t w = 0;
+  w = fp4x2_rn<0>(w, v[0], v[1]);
+  w = fp4x2_rn<1>(w, v[2], v[3]);
+  w = fp4x2_rn<2>(w, v[4], v[5]);
+  w = fp4x2_rn<3>(w, v[6], v[7]);
+  return w;
+}
+
+// Stochastic rounding of one scaled value v to an E2M1 code [Review s10 SR
+// formula; s7 SR example]: with lo <= |v| < hi the neighbouring grid values,
+// round up iff r16 < (|v| - lo)/(hi - lo) * 65536.  For |v| in [1, 6) the
+// fraction is exactly the fp32 mantissa bits below the E2M1 mantissa bit,
+// so the test is an integer compare.
+__device__ __forceinline__ uint32_t fp4_sr(float v, uint32_t r16) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+  const float m = __builtin_fabsf(v);
+  uint32_t idx;
+  if (m >= 6.0f) {
+    idx = 7u;
+  } else if (m >= 1.0f) {
+    const uint32_t bits = __float_as_uint(m);
+    idx = (bits >> 22) - 252u + ((r16 << 6) < (bits & 0x3FFFFFu) ? 1u : 0u);
+  } else {
+    const uint32_t lo = m >= 0.5f ? 1u : 0u;
+    const float frac = (m - (lo ? 0.5f : 0.0f)) * 2.0f;
+    idx = lo + ((float)r16 < frac * 65536.0f ? 1u : 0u);
+  }
+  return sign | idx;
+}
+
+// ---------------------------------------------------------------- Philox
+
+// Philox4x32-10 (Salmon, Moraes, Dror & Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies with Weyl-sequence key bumps.
+struct U4 {
+  uint32_t x, y, z, w;
+};
+__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                            uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
+// The eight 16-bit draws of elements e .. e+7 (e % 8 == 0) of one operand.
+__device__ __forceinline__ U4 sr_draw8(uint64_t seed, uint32_t stream, uint64_t e) {
+  const uint64_t j = e >> 3;
+  return philox4x32_10((uint32_t)j, (uint32_t)(j >> 32), stream, 0u, (uint32_t)seed,
+                       (uint32_t)(seed >> 32));
+}
+
+// Eight values -> eight SR codes using the eight draws in r.
+__device__ __forceinline__ uint32_t fp4x8_sr(const float* v, const U4& r) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t r16 = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+    out |= fp4_sr(v[i], r16) << (4 * i);
+  }
+  return out;
+}
+
+// ---------------------------------------------------------------- RHT16
+
+// In-place 16-point transform y = 1/4 H16 diag(s) x on u[0..15] with stride
+// S [Review s3]: signs, butterflies h = 1, 2, 4, 8 as (a+b, a-b), x 1/4.
+template <int S>
+__device__ __forceinline__ void rht16_inplace(float* u, uint32_t signs) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if ((signs >> i) & 1u) u[i * S] = -u[i * S];
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = u[i * S], b = u[(i + h) * S];
+      u[i * S] = a + b;
+      u[(i + h) * S] = a - b;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u[i * S] = u[i * S] * 0.25f;
+}
+
+// ---------------------------------------------------------------- bf16 out
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > kInfBits) return (uint16_t)((b >> 16) | 0x40u);  // quiet NaN
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+}  // namespace nvfp4

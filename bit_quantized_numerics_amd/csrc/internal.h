@@ -1,0 +1,56 @@
+// internal.h -- launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+
+// Tile-quantiser feature flags.
+constexpr int kFRow = 1;     // emit the row-wise copy (1x16 along cols, or 16x16)
+constexpr int kFCol = 2;     // emit the column-wise copy (operand = x^T)
+constexpr int kF2D = 4;      // 16x16 blocks (weights); the column copy is the transpose
+constexpr int kFRht = 8;     // RHT16 along rows before the column copy
+constexpr int kFSrRow = 16;  // stochastic rounding for the row copy
+constexpr int kFSrCol = 32;  // stochastic rounding for the column copy
+
+struct CopyArgs {
+  uint8_t* codes = nullptr;
+  uint8_t* scales = nullptr;
+  float* global = nullptr;
+  const uint32_t* amax = nullptr;  // device word holding the copy's amax bits
+  uint64_t seed = 0;
+  uint64_t offset = 0;
+  uint32_t stream = 0;
+};
+
+struct TileArgs {
+  const void* x = nullptr;
+  int64_t rows = 0, cols = 0, ld = 0;
+  CopyArgs row, col;
+  uint32_t signs = 0;
+  uint32_t* status = nullptr;
+};
+
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t s);
+hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       uint32_t signs, uint32_t* out_raw, uint32_t* out_rht, hipStream_t s);
+hipError_t launch_quant_tile(int dtype, int flags, const TileArgs& a, hipStream_t s);
+hipError_t launch_rht16(const void* x, float* y, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                        int axis, uint32_t signs, hipStream_t s);
+
+struct GemmOperand {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* global;
+  int64_t rows;
+  int scale_shift;  // 0: one scale row per operand row; 4: per 16 rows (16x16)
+};
+
+hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c,
+                       int c_dtype, int64_t ldc, hipStream_t s);
+
+}  // namespace nvfp4

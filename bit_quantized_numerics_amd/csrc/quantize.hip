@@ -1,0 +1,401 @@
+// quantize.hip -- NVFP4 quantisation kernels for gfx950.
+//
+// Citations: [Review] = web page "NVFP4 4-bit Pretraining, Made Practical: 12B
+// up to 10T Tokens, Effectively On Par with FP8" (review of arXiv 2509.25149),
+// by numbered section; [Captions] = that paper's figure-caption list.
+//
+// Work decomposition.  Every kernel walks the source matrix x [rows, cols]
+// (row-major, cols contiguous) in tiles of 256 rows x 128 columns; each of
+// the 256 threads of a workgroup owns one 16-row x 8-column patch.  That
+// patch shape serves every block geometry of the layer:
+//   - a 1x16 block along cols is one row of the patch plus the neighbouring
+//     lane's row (lane ^ 1 holds the other 8 columns);
+//   - a 1x16 block along rows (the column-wise copy the backward GEMMs need,
+//     [Review s2]) is one column of the patch, which is also exactly one
+//     16-token chunk of the random Hadamard transform [Review s3];
+//   - a 16x16 weight tile is the patch plus its neighbour lane's patch.
+// Reads are 16-byte loads, 16 per thread in flight; the column-wise copy is
+// staged in LDS so that each output row segment is written contiguously.
+#include "device_common.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+constexpr int kTileR = 256;  // source rows per workgroup
+constexpr int kTileC = 128;  // source cols per workgroup
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------- zero
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t s) {
+  hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- patch load
+
+template <typename TIn>
+__device__ __forceinline__ void load_patch(const TIn* x, int64_t rows, int64_t ld, int64_t r0,
+                                           int64_t c0, bool valid, float (&v)[16][8]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (valid && r0 + i < rows) {
+      load8(x + (r0 + i) * ld + c0, v[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- stats
+// Tensor amax [Review s1 Step 1] as the largest |x| bit pattern (Inf/NaN sort
+// above every finite value, so a non-finite input is never lost), and with
+// RHTC also the amax of the transform along rows (the Wgrad copies take their
+// scale after the transform).
+
+template <typename TIn, bool RAW, bool RHTC>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const TIn* __restrict__ x, int64_t rows,
+                                                        int64_t cols, int64_t ld, uint32_t signs,
+                                                        uint32_t* out_raw, uint32_t* out_rht) {
+  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
+  const int64_t r0 = (int64_t)blockIdx.y * kTileR + rs * 16;
+  const int64_t c0 = (int64_t)blockIdx.x * kTileC + cg * 8;
+  const bool valid = r0 < rows && c0 < cols;
+  float v[16][8];
+  load_patch(x, rows, ld, r0, c0, valid, v);
+  uint32_t m_raw = 0, m_rht = 0;
+  if (RAW) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t b = __float_as_uint(v[i][j]) & 0x7FFFFFFFu;
+        m_raw = m_raw > b ? m_raw : b;
+      }
+  }
+  if (RHTC) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rht16_inplace<8>(&v[0][j], signs);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t b = __float_as_uint(v[i][j]) & 0x7FFFFFFFu;
+        m_rht = m_rht > b ? m_rht : b;
+      }
+  }
+  if (RAW) m_raw = wave_max_u32(m_raw);
+  if (RHTC) m_rht = wave_max_u32(m_rht);
+  if ((t & 63) == 0) {
+    if (RAW) atomicMax(out_raw, m_raw);
+    if (RHTC) atomicMax(out_rht, m_rht);
+  }
+}
+
+template <typename TIn>
+static hipError_t amax_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                                uint32_t signs, uint32_t* out_raw, uint32_t* out_rht,
+                                hipStream_t s) {
+  const dim3 grid((unsigned)((cols + kTileC - 1) / kTileC), (unsigned)((rows + kTileR - 1) / kTileR));
+  const TIn* p = static_cast<const TIn*>(x);
+  if (out_raw && out_rht)
+    hipLaunchKernelGGL((amax_kernel<TIn, true, true>), grid, dim3(kThreads), 0, s, p, rows, cols, ld,
+                       signs, out_raw, out_rht);
+  else if (out_raw)
+    hipLaunchKernelGGL((amax_kernel<TIn, true, false>), grid, dim3(kThreads), 0, s, p, rows, cols,
+                       ld, signs, out_raw, out_rht);
+  else
+    hipLaunchKernelGGL((amax_kernel<TIn, false, true>), grid, dim3(kThreads), 0, s, p, rows, cols,
+                       ld, signs, out_raw, out_rht);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       uint32_t signs, uint32_t* out_raw, uint32_t* out_rht, hipStream_t s) {
+  if (dtype == kDtypeBF16) return amax_dispatch<uint16_t>(x, rows, cols, ld, signs, out_raw, out_rht, s);
+  return amax_dispatch<float>(x, rows, cols, ld, signs, out_raw, out_rht, s);
+}
+
+// ---------------------------------------------------------------- emit
+
+// Reads one copy's amax word; flags the status word and returns false when
+// the amax is not finite (that copy is then skipped).
+__device__ __forceinline__ bool copy_scales(const uint32_t* amax, uint32_t* status,
+                                            TensorScales* ts) {
+  const uint32_t bits = *amax;
+  if (bits >= kInfBits) {
+    if (threadIdx.x == 0) atomicMax(status, kStatusNonfinite);
+    return false;
+  }
+  *ts = tensor_scales(bits);
+  return true;
+}
+
+template <typename TIn, int F>
+__global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
+  constexpr bool ROW = F & kFRow, COL = F & kFCol, TWO_D = F & kF2D, RHT = F & kFRht;
+  constexpr bool SR_ROW = F & kFSrRow, SR_COL = F & kFSrCol;
+  constexpr int kPitch = kTileR / 2 + 8;  // LDS row pitch (bytes) of the staged column copy
+  __shared__ __align__(16) uint8_t lds_codes[COL ? kTileC : 1][COL ? kPitch : 8];
+  __shared__ uint8_t lds_scales[(COL && !TWO_D) ? kTileC : 1][kTileR / 16];
+
+  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
+  const int64_t rows = a.rows, cols = a.cols;
+  const int64_t tile_r0 = (int64_t)blockIdx.y * kTileR, tile_c0 = (int64_t)blockIdx.x * kTileC;
+  const int64_t r0 = tile_r0 + rs * 16, c0 = tile_c0 + cg * 8;
+  const bool valid = r0 < rows && c0 < cols;
+
+  TensorScales tr{}, tc{};
+  bool do_row = false, do_col = false;
+  if (ROW) do_row = copy_scales(a.row.amax, a.status, &tr);
+  if (COL) {
+    if (TWO_D) {
+      do_col = do_row;
+      tc = tr;
+    } else {
+      do_col = copy_scales(a.col.amax, a.status, &tc);
+    }
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
+    if (do_row) *a.row.global = tr.g;
+    if (do_col && a.col.global) *a.col.global = tc.g;
+  }
+  if (!do_row && !do_col) return;  // uniform across the workgroup
+
+  float v[16][8];
+  load_patch(static_cast<const TIn*>(a.x), rows, a.ld, r0, c0, valid, v);
+
+  if (TWO_D) {
+    // ---- one scale per 16x16 tile [Review s2]: this patch and lane ^ 1's
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, __builtin_fabsf(v[i][j]));
+    am = fmaxf(am, lane_xor1(am));
+    uint32_t dcode;
+    const float r = block_scale(am, tr, &dcode);
+    if (valid) {
+      const int64_t gcols = cols / 16, grows = rows / 16;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float s[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[j] = v[i][j] * r;
+        *reinterpret_cast<uint32_t*>(a.row.codes + (r0 + i) * (cols / 2) + c0 / 2) = fp4x8_rn(s);
+      }
+      if ((cg & 1) == 0) {
+        a.row.scales[(r0 / 16) * gcols + c0 / 16] = (uint8_t)dcode;
+        if (COL) a.col.scales[(c0 / 16) * grows + r0 / 16] = (uint8_t)dcode;
+      }
+      if (COL) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float s[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[i] = v[i][j] * r;
+          uint2 w;
+          w.x = fp4x8_rn(s);
+          w.y = fp4x8_rn(s + 8);
+          *reinterpret_cast<uint2*>(&lds_codes[cg * 8 + j][rs * 8]) = w;
+        }
+      }
+    }
+  } else {
+    // ---- row-wise copy: 1x16 blocks along cols [Review s1 Steps 2-3]
+    if (ROW && do_row) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float am = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = fmaxf(am, __builtin_fabsf(v[i][j]));
+        am = fmaxf(am, lane_xor1(am));
+        uint32_t dcode;
+        const float r = block_scale(am, tr, &dcode);
+        if (valid && r0 + i < rows) {
+          float s[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s[j] = v[i][j] * r;
+          uint32_t w;
+          if (SR_ROW)
+            w = fp4x8_sr(s, sr_draw8(a.row.seed, a.row.stream,
+                                     a.row.offset + (uint64_t)((r0 + i) * cols + c0)));
+          else
+            w = fp4x8_rn(s);
+          *reinterpret_cast<uint32_t*>(a.row.codes + (r0 + i) * (cols / 2) + c0 / 2) = w;
+          if ((cg & 1) == 0) a.row.scales[(r0 + i) * (cols / 16) + c0 / 16] = (uint8_t)dcode;
+        }
+      }
+    }
+    // ---- column-wise copy: 1x16 blocks along rows, optional RHT [Review s3]
+    if (COL && do_col) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (RHT) rht16_inplace<8>(&v[0][j], a.signs);
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) am = fmaxf(am, __builtin_fabsf(v[i][j]));
+        uint32_t dcode;
+        const float r = block_scale(am, tc, &dcode);
+        float s[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = v[i][j] * r;
+        uint2 w;
+        if (SR_COL) {
+          const uint64_t e = a.col.offset + (uint64_t)((c0 + j) * rows + r0);
+          w.x = fp4x8_sr(s, sr_draw8(a.col.seed, a.col.stream, e));
+          w.y = fp4x8_sr(s + 8, sr_draw8(a.col.seed, a.col.stream, e + 8));
+        } else {
+          w.x = fp4x8_rn(s);
+          w.y = fp4x8_rn(s + 8);
+        }
+        *reinterpret_cast<uint2*>(&lds_codes[cg * 8 + j][rs * 8]) = w;
+        lds_scales[cg * 8 + j][rs] = (uint8_t)dcode;
+      }
+    }
+  }
+
+  if (COL) {
+    __syncthreads();
+    if (do_col) {
+      // operand = x^T: row gr (a source column) holds rows/2 code bytes
+      const int64_t pitch = rows / 2;
+#pragma unroll
+      for (int q = t; q < kTileC * 16; q += kThreads) {
+        const int orow = q >> 4, p = q & 15;
+        const int64_t gr = tile_c0 + orow, ge = tile_r0 + p * 16;
+        if (gr < cols && ge < rows)
+          *reinterpret_cast<uint2*>(a.col.codes + gr * pitch + ge / 2) =
+              *reinterpret_cast<const uint2*>(&lds_codes[orow][p * 8]);
+      }
+      if (!TWO_D) {
+        const int64_t spitch = rows / 16;
+#pragma unroll
+        for (int q = t; q < kTileC * 16; q += kThreads) {
+          const int orow = q >> 4, p = q & 15;
+          const int64_t gr = tile_c0 + orow, ge = tile_r0 + p * 16;
+          if (gr < cols && ge < rows) a.col.scales[gr * spitch + ge / 16] = lds_scales[orow][p];
+        }
+      }
+    }
+  }
+}
+
+template <typename TIn, int F>
+static void launch_tile(const TileArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.cols + kTileC - 1) / kTileC),
+                  (unsigned)((a.rows + kTileR - 1) / kTileR));
+  hipLaunchKernelGGL((quant_tile_kernel<TIn, F>), grid, dim3(kThreads), 0, s, a);
+}
+
+template <typename TIn>
+static bool tile_dispatch(int flags, const TileArgs& a, hipStream_t s) {
+  switch (flags) {
+#define NVFP4_CASE(F) \
+  case (F):           \
+    launch_tile<TIn, (F)>(a, s); \
+    return true;
+    NVFP4_CASE(kFRow)
+    NVFP4_CASE(kFRow | kFSrRow)
+    NVFP4_CASE(kFCol)
+    NVFP4_CASE(kFCol | kFSrCol)
+    NVFP4_CASE(kFCol | kFRht)
+    NVFP4_CASE(kFCol | kFRht | kFSrCol)
+    NVFP4_CASE(kFRow | kFCol)
+    NVFP4_CASE(kFRow | kFCol | kFRht)
+    NVFP4_CASE(kFRow | kFCol | kFSrRow | kFSrCol)
+    NVFP4_CASE(kFRow | kFCol | kFRht | kFSrRow | kFSrCol)
+    NVFP4_CASE(kFRow | kFCol | kFSrRow)
+    NVFP4_CASE(kFRow | kFCol | kFRht | kFSrRow)
+    NVFP4_CASE(kFRow | kFCol | kFSrCol)
+    NVFP4_CASE(kFRow | kFCol | kFRht | kFSrCol)
+    NVFP4_CASE(kFRow | kF2D)
+    NVFP4_CASE(kFRow | kFCol | kF2D)
+#undef NVFP4_CASE
+    default:
+      return false;
+  }
+}
+
+hipError_t launch_quant_tile(int dtype, int flags, const TileArgs& a, hipStream_t s) {
+  const bool ok = dtype == kDtypeBF16 ? tile_dispatch<uint16_t>(flags, a, s)
+                                      : tile_dispatch<float>(flags, a, s);
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RHT16
+// Standalone transform [Review s3] to dense fp32.  axis 0: each thread
+// transforms the 8 columns of a 16-row patch; axis 1: each thread transforms
+// one 16-element row chunk.
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void rht16_axis0_kernel(const TIn* __restrict__ x,
+                                                               float* __restrict__ y, int64_t rows,
+                                                               int64_t cols, int64_t ld,
+                                                               uint32_t signs) {
+  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
+  const int64_t r0 = (int64_t)blockIdx.y * kTileR + rs * 16;
+  const int64_t c0 = (int64_t)blockIdx.x * kTileC + cg * 8;
+  const bool valid = r0 < rows && c0 < cols;
+  if (!valid) return;
+  float v[16][8];
+  load_patch(x, rows, ld, r0, c0, valid, v);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rht16_inplace<8>(&v[0][j], signs);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float4* o = reinterpret_cast<float4*>(y + (r0 + i) * cols + c0);
+    o[0] = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+    o[1] = make_float4(v[i][4], v[i][5], v[i][6], v[i][7]);
+  }
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void rht16_axis1_kernel(const TIn* __restrict__ x,
+                                                               float* __restrict__ y, int64_t rows,
+                                                               int64_t cols, int64_t ld,
+                                                               uint32_t signs) {
+  const int64_t chunks_per_row = cols / 16;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= rows * chunks_per_row) return;
+  const int64_t r = idx / chunks_per_row, c = (idx % chunks_per_row) * 16;
+  float u[16];
+  load8(x + r * ld + c, u);
+  load8(x + r * ld + c + 8, u + 8);
+  rht16_inplace<1>(u, signs);
+  float4* o = reinterpret_cast<float4*>(y + r * cols + c);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = make_float4(u[4 * k], u[4 * k + 1], u[4 * k + 2], u[4 * k + 3]);
+}
+
+hipError_t launch_rht16(const void* x, float* y, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                        int axis, uint32_t signs, hipStream_t s) {
+  if (axis == 0) {
+    const dim3 grid((unsigned)((cols + kTileC - 1) / kTileC), (unsigned)((rows + kTileR - 1) / kTileR));
+    if (dtype == kDtypeBF16)
+      hipLaunchKernelGGL(rht16_axis0_kernel<uint16_t>, grid, dim3(kThreads), 0, s,
+                         static_cast<const uint16_t*>(x), y, rows, cols, ld, signs);
+    else
+      hipLaunchKernelGGL(rht16_axis0_kernel<float>, grid, dim3(kThreads), 0, s,
+                         static_cast<const float*>(x), y, rows, cols, ld, signs);
+  } else {
+    const int64_t n = rows * (cols / 16);
+    const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+    if (dtype == kDtypeBF16)
+      hipLaunchKernelGGL(rht16_axis1_kernel<uint16_t>, grid, dim3(kThreads), 0, s,
+                         static_cast<const uint16_t*>(x), y, rows, cols, ld, signs);
+    else
+      hipLaunchKernelGGL(rht16_axis1_kernel<float>, grid, dim3(kThreads), 0, s,
+                         static_cast<const float*>(x), y, rows, cols, ld, signs);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

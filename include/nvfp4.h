@@ -1,0 +1,242 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 linear-layer library.
+ *
+ * NVFP4 is the two-level 4-bit format of "Pretraining Large Language Models
+ * with NVFP4" (arXiv 2509.25149).  Citations below name two web pages about
+ * that paper:
+ *   [Review]   "NVFP4 4-bit Pretraining, Made Practical: 12B up to 10T Tokens,
+ *              Effectively On Par with FP8" (jaehun.me paper review), by its
+ *              numbered sections ("s1 Step 2" = second step of section
+ *              "1) The NVFP4 quantization pipeline").
+ *   [Captions] the paper's figure-caption list, by figure number.
+ *
+ * Format of one quantised operand [rows, cols] (cols = contraction / block axis):
+ *   codes   uint8 [rows][cols/2]; two E2M1 codes per byte, the even column in
+ *           the low nibble; code = sign << 3 | magnitude index, magnitudes
+ *           {0, .5, 1, 1.5, 2, 3, 4, 6}                     [Review s7]
+ *   scales  uint8 E4M3 (OCP E4M3FN bit pattern) decode scales, one per block:
+ *           1x16 mode  [rows][cols/16]  (16 consecutive elements of a row)
+ *           16x16 mode [rows/16][cols/16] (one per 16x16 tile)  [Review s2]
+ *   global  one fp32 g = 1/s_enc with s_enc = 2688/amax (6 x 448)
+ *                                                    [Review s1 Step 1]
+ *   value   x_hat = e2m1(code) * e4m3(scale) * g     [Review s1 Step 3]
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers; the caller owns every buffer.
+ *     The library never allocates device memory and keeps no global state.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work on it and return; none synchronises except
+ *     nvfp4_device_status().
+ *   - Argument errors are returned synchronously and then NOTHING has been
+ *     enqueued.  A failed launch returns NVFP4_ERR_HIP.  A non-finite tensor
+ *     amax is only known on the device: the kernels then record
+ *     NVFP4_ERR_NONFINITE in the workspace's status word (read it with
+ *     nvfp4_device_status) and that operand's outputs are unspecified.
+ *   - `workspace` is a device buffer of at least nvfp4_workspace_bytes()
+ *     bytes holding the status word and per-call reduction slots.  Calls that
+ *     share a workspace must be issued on one stream (they reuse its slots).
+ *   - Shapes: rows and cols are multiples of 16 except where stated; leading
+ *     dimensions are in elements and >= cols; device pointers must be 16-byte
+ *     aligned and ld * element size a multiple of 16 bytes.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,       /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,      /* sizes not supported / inconsistent */
+  NVFP4_ERR_ALIGN = 3,      /* pointer, leading dimension or offset misaligned */
+  NVFP4_ERR_DTYPE = 4,      /* unsupported dtype or enum value */
+  NVFP4_ERR_WORKSPACE = 5,  /* workspace missing or too small */
+  NVFP4_ERR_HIP = 6,        /* a HIP launch or runtime call failed */
+  NVFP4_ERR_NONFINITE = 7   /* device-side: an operand's amax is Inf/NaN */
+} nvfp4_status;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
+typedef enum { NVFP4_RN = 0, NVFP4_SR = 1 } nvfp4_round;
+typedef enum { NVFP4_SCALE_1X16 = 0, NVFP4_SCALE_16X16 = 1 } nvfp4_scale_mode;
+
+/* One quantised operand (see the format above).  rows x cols is the
+ * operand's own logical shape; cols is the block (contraction) axis. */
+typedef struct {
+  uint8_t* codes;
+  uint8_t* scales;
+  float* global_scale; /* device pointer to one fp32 (g = 1/s_enc) */
+  int64_t rows;
+  int64_t cols;
+  int32_t scale_mode;  /* nvfp4_scale_mode */
+} nvfp4_tensor;
+
+/* Options of one 1x16 quantisation.
+ *   round      NVFP4_RN: nearest-even (activations, weights)
+ *              NVFP4_SR: stochastic (gradients)      [Review s1 Step 3, s4]
+ *   transpose  0: the operand is x [rows, cols], blocks along cols;
+ *              1: the operand is x^T [cols, rows], blocks along x's rows
+ *                 (tokens) -- the column-wise copy the backward GEMMs need
+ *                 because the contraction axis flips      [Review s2]
+ *   rht        1: apply the 16-point random Hadamard transform to each
+ *              16-element chunk along the operand's block axis first
+ *              (Wgrad inputs only in the recipe)           [Review s3]
+ *   rht_signs  sign diagonal, bit i set = s_i is -1
+ *   seed, offset, stream_id
+ *              stochastic-rounding draw of operand element (r, c) comes from
+ *              the Philox4x32-10 counter-based generator with key = seed,
+ *              counter = (e/8, stream_id, 0), e = offset + r*C + c in the
+ *              operand's own [R, C] layout; offset % 16 == 0. */
+typedef struct {
+  int32_t round;
+  int32_t transpose;
+  int32_t rht;
+  uint32_t rht_signs;
+  uint64_t seed;
+  uint64_t offset;
+  uint32_t stream_id;
+} nvfp4_quant_opts;
+
+/* The pages' layer recipe [Review "Core idea" items (2)-(4); Captions
+ * Fig. 5]: 16x16 weight scales, RHT on the Wgrad inputs only, stochastic
+ * rounding on the gradient copies only.  Defaults via nvfp4_recipe_default. */
+typedef struct {
+  uint32_t rht_signs;   /* sign diagonal shared by every RHT of the layer */
+  int32_t training;     /* forward also builds the Wgrad copy of X */
+} nvfp4_recipe;
+
+/* Buffers of one layer step Y = X W^T, X [M, K], W [N, K], dY [M, N].
+ * The caller allocates each operand with nvfp4_tensor_bytes() and fills
+ * codes/scales/global_scale pointers; shapes are set by the library.
+ *   xq   X       [M, K] 1x16 RN          (Fprop A)
+ *   wq   W       [N, K] 16x16 RN         (Fprop B)
+ *   wqt  W^T     [K, N] 16x16 RN, same codes transposed, same g (Dgrad B)
+ *   xqt  (R X)^T [K, M] 1x16 along tokens, RHT, RN              (Wgrad B)
+ *   dyq  dY      [M, N] 1x16 SR, stream 0                       (Dgrad A)
+ *   dyqt (R dY)^T [N, M] 1x16 along tokens, RHT, SR, stream 1   (Wgrad A) */
+typedef struct {
+  int64_t M, K, N;
+  nvfp4_tensor xq, wq, wqt, xqt, dyq, dyqt;
+} nvfp4_linear_ctx;
+
+/* ------------------------------------------------------------ size queries */
+
+/* Bytes of the codes and scales arrays of a [rows, cols] operand. */
+nvfp4_status nvfp4_tensor_bytes(int64_t rows, int64_t cols, int32_t scale_mode,
+                                size_t* codes_bytes, size_t* scales_bytes);
+
+/* Minimum workspace size in bytes (a small constant). */
+size_t nvfp4_workspace_bytes(void);
+
+/* Host-side: the sign diagonal from a seed = low 16 bits of word 0 of
+ * Philox4x32-10(counter 0, key = seed)  [Review s3: one fixed seed]. */
+uint32_t nvfp4_rht_signs_from_seed(uint64_t seed);
+
+/* Zero the workspace (status word and slots) on `stream`. */
+nvfp4_status nvfp4_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+/* Synchronises `stream`, returns the device status word (NVFP4_OK or
+ * NVFP4_ERR_NONFINITE) and clears it. */
+nvfp4_status nvfp4_device_status(void* workspace, void* stream);
+
+const char* nvfp4_status_string(nvfp4_status s);
+
+/* -------------------------------------------------------------- operations */
+
+/*
+ * nvfp4_quantize: two-level NVFP4 quantisation of one operand with 1x16
+ * blocks [Review s1 Steps 1-3; Captions Fig. 1]:
+ *   1. tensor amax A of the operand (after the RHT when opts->rht),
+ *      s_enc = 2688/A (FLT_MAX if that overflows; 1 when A == 0), g = 1/s_enc;
+ *   2. per block: d_b = E4M3(amax_b * (s_enc/6)), nearest-even, saturating;
+ *   3. per element: v = x * (s_enc/d_b), E2M1 code of v by opts->round.
+ * x: [rows, cols] of `dtype` (NVFP4_F32 or NVFP4_BF16), leading dim ld.
+ * out: operand [rows, cols] (transpose 0) or [cols, rows] (transpose 1);
+ *      out->rows/cols/scale_mode are set by the call.
+ * Ragged rows (rows % 16 != 0) are allowed for transpose 0 without RHT.
+ */
+nvfp4_status nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                            int64_t ld, const nvfp4_quant_opts* opts, nvfp4_tensor* out,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_quantize_rowcol: both copies an operand needs for a training step
+ * from one read of x [rows, cols]: `row` = x with 1x16 blocks along cols
+ * (opts_row; transpose/rht must be 0) and `col` = (R x)^T with 1x16 blocks
+ * along rows (opts_col; transpose must be 1, rht optional).  Each copy has its
+ * own tensor scale.  Equivalent to two nvfp4_quantize calls.  [Review s6
+ * steps 1-3; Captions Fig. 5]
+ */
+nvfp4_status nvfp4_quantize_rowcol(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                   int64_t ld, const nvfp4_quant_opts* opts_row,
+                                   const nvfp4_quant_opts* opts_col, nvfp4_tensor* row,
+                                   nvfp4_tensor* col, void* workspace, size_t ws_bytes,
+                                   void* stream);
+
+/*
+ * nvfp4_quantize_2d: weight quantisation with one E4M3 scale per 16x16 tile
+ * and nearest-even rounding [Review s2; "Core idea" item (2)].  out = W
+ * [rows, cols] with grid [rows/16][cols/16]; out_t (nullable) = the same
+ * codes transposed, [cols, rows] with grid [cols/16][rows/16] and the same
+ * g, so the backward GEMM sees exactly the forward weight.
+ */
+nvfp4_status nvfp4_quantize_2d(const void* w, int32_t dtype, int64_t rows, int64_t cols,
+                               int64_t ld, nvfp4_tensor* out, nvfp4_tensor* out_t,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_rht16: standalone 16-point random Hadamard transform
+ * y = 1/4 * H16 * diag(s) * x on every 16-element chunk [Review s3].
+ * axis 1: chunks along each row (cols % 16 == 0); axis 0: along each column
+ * (rows % 16 == 0).  x: [rows, cols] F32 or BF16 with leading dim ld;
+ * y: dense fp32 [rows, cols].  fp32 order: signs, butterflies h = 1, 2, 4, 8
+ * as (a+b, a-b), then x 1/4.
+ */
+nvfp4_status nvfp4_rht16(const void* x, float* y, int32_t in_dtype, int64_t rows,
+                         int64_t cols, int64_t ld, int32_t axis, uint32_t rht_signs,
+                         void* stream);
+
+/*
+ * nvfp4_gemm: C[m][n] = g_a g_b sum_k (e2m1*d_b)_A[m][k] (e2m1*d_b)_B[n][k]
+ * with FP32 accumulation [Review s6 step 1; Captions Fig. 5].  Both operands
+ * are contiguous along k (a->cols == b->cols == K); either may use 1x16 or
+ * 16x16 scales.  c: [M, N] row-major with leading dim ldc, dtype NVFP4_F32 or
+ * NVFP4_BF16.  M, N multiples of 16; K a multiple of 16.
+ */
+nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int32_t c_dtype,
+                        int64_t ldc, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_linear_fwd: forward of one NVFP4 linear layer Y = X W^T [Review s6
+ * step 1; Captions Fig. 5].  Quantises X (1x16 RN -> ctx->xq), W (16x16 RN ->
+ * ctx->wq and ctx->wqt) and, when recipe->training, (R X)^T (RHT along
+ * tokens, RN -> ctx->xqt), then runs the Fprop GEMM.  x [M, K], w [N, K] of
+ * `dtype`, dense; y [M, N] bf16.  M, K, N multiples of 16.
+ */
+nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, int64_t K,
+                              int64_t N, int32_t dtype, const nvfp4_recipe* recipe,
+                              nvfp4_linear_ctx* ctx, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * nvfp4_linear_bwd: backward of the same layer [Review s6 steps 2-3;
+ * Captions Fig. 5].  Quantises dY twice from one read: dY 1x16 SR stream 0
+ * (ctx->dyq) and (R dY)^T with the RHT along tokens, SR stream 1
+ * (ctx->dyqt), both with key sr_seed; then Dgrad dX = dyq . wqt^T (bf16
+ * [M, K]) and Wgrad dW = dyqt . xqt^T ([N, K], dw_dtype F32 or BF16).
+ * Requires a preceding nvfp4_linear_fwd with recipe->training on ctx.
+ */
+nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* ctx, void* dx,
+                              void* dw, int32_t dw_dtype, uint64_t sr_seed,
+                              const nvfp4_recipe* recipe, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

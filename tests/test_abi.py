@@ -1,0 +1,116 @@
+"""CPU tests of the C ABI: the library loads, exports every function
+include/nvfp4.h declares, sizes are right, and argument errors are returned
+before anything is enqueued (no GPU needed: no call here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_numerics_amd as nv
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(nv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(nv.EXPORTED)
+
+
+def test_tensor_bytes():
+    assert nv.nvfp4_tensor_bytes(64, 256, nv.SCALE_1X16) == (64 * 128, 64 * 16)
+    assert nv.nvfp4_tensor_bytes(128, 256, nv.SCALE_16X16) == (128 * 128, 8 * 16)
+    for bad in [(64, 24, 0), (0, 16, 0), (24, 32, 1), (16, 16, 5)]:
+        with pytest.raises(nv.NVFP4Error):
+            nv.nvfp4_tensor_bytes(*bad)
+
+
+def test_workspace_bytes_and_status_strings():
+    assert nv.nvfp4_workspace_bytes() >= 64
+    for s in range(8):
+        assert nv.nvfp4_status_string(s)
+
+
+def test_rht_signs_from_seed_matches_generator_definition():
+    for seed in [0, 1, 1234, 2**40 + 7]:
+        assert nv.nvfp4_rht_signs_from_seed(seed) == O.rht_signs_from_seed(seed)
+
+
+# Fake but non-null, suitably aligned device addresses: every case below must
+# be rejected by validation before any HIP call.
+P = 1 << 20
+
+
+def _tensor(codes=P, scales=P, glob=P):
+    return nv.c_tensor(codes, scales, glob, 0, 0, 0)
+
+
+def _q(x=P, dtype=nv.BF16, rows=64, cols=256, ld=256, opts=None, out=None, ws=P, wsb=256):
+    o = opts or nv.c_quant_opts(0, 0, 0, 0, 0, 0, 0)
+    t = out or _tensor()
+    return nv._lib.nvfp4_quantize(x, dtype, rows, cols, ld, ctypes.byref(o), ctypes.byref(t), ws,
+                                  wsb, None)
+
+
+def test_quantize_argument_errors():
+    assert _q(x=None) == nv.ERR_NULL
+    assert _q(out=_tensor(codes=None)) == nv.ERR_NULL
+    assert _q(dtype=7) == nv.ERR_DTYPE
+    assert _q(cols=24, ld=24) == nv.ERR_SHAPE
+    assert _q(rows=0) == nv.ERR_SHAPE
+    assert _q(ld=128) == nv.ERR_SHAPE
+    assert _q(x=P + 2) == nv.ERR_ALIGN
+    assert _q(ld=260) == nv.ERR_ALIGN
+    assert _q(out=_tensor(codes=P + 4)) == nv.ERR_ALIGN
+    assert _q(ws=None) == nv.ERR_WORKSPACE
+    assert _q(wsb=16) == nv.ERR_WORKSPACE
+    assert _q(opts=nv.c_quant_opts(2, 0, 0, 0, 0, 0, 0)) == nv.ERR_DTYPE
+    assert _q(opts=nv.c_quant_opts(1, 0, 0, 0, 0, 8, 0)) == nv.ERR_ALIGN       # offset % 16
+    assert _q(opts=nv.c_quant_opts(0, 0, 1, 0, 0, 0, 0)) == nv.ERR_SHAPE       # RHT needs transpose
+    assert _q(rows=40, opts=nv.c_quant_opts(0, 1, 0, 0, 0, 0, 0)) == nv.ERR_SHAPE
+    assert _q(opts=nv.c_quant_opts(0, 1, 1, 0x10000, 0, 0, 0)) == nv.ERR_DTYPE
+
+
+def test_gemm_argument_errors():
+    a = nv.c_tensor(P, P, P, 64, 256, 0)
+    b = nv.c_tensor(P, P, P, 128, 256, 1)
+    f = nv._lib.nvfp4_gemm
+    assert f(ctypes.byref(a), ctypes.byref(b), None, nv.F32, 128, None, 0, None) == nv.ERR_NULL
+    bad_k = nv.c_tensor(P, P, P, 128, 240, 0)
+    assert f(ctypes.byref(a), ctypes.byref(bad_k), P, nv.F32, 128, None, 0, None) == nv.ERR_SHAPE
+    assert f(ctypes.byref(a), ctypes.byref(b), P, 9, 128, None, 0, None) == nv.ERR_DTYPE
+    assert f(ctypes.byref(a), ctypes.byref(b), P, nv.F32, 64, None, 0, None) == nv.ERR_SHAPE
+    b2 = nv.c_tensor(P, P, P, 120, 256, 1)  # 16x16 mode needs rows % 16
+    assert f(ctypes.byref(a), ctypes.byref(b2), P, nv.F32, 128, None, 0, None) == nv.ERR_SHAPE
+    a_mis = nv.c_tensor(P + 8, P, P, 64, 256, 0)
+    assert f(ctypes.byref(a_mis), ctypes.byref(b), P, nv.F32, 128, None, 0, None) == nv.ERR_ALIGN
+
+
+def test_2d_rht_and_layer_argument_errors():
+    t = _tensor()
+    assert nv._lib.nvfp4_quantize_2d(P, nv.BF16, 40, 32, 32, ctypes.byref(t), None, P, 256,
+                                     None) == nv.ERR_SHAPE
+    assert nv._lib.nvfp4_rht16(P, P, nv.F32, 24, 32, 32, 0, 0, None) == nv.ERR_SHAPE
+    assert nv._lib.nvfp4_rht16(P, P, nv.F32, 32, 24, 24, 1, 0, None) == nv.ERR_SHAPE
+    assert nv._lib.nvfp4_rht16(None, P, nv.F32, 32, 32, 32, 1, 0, None) == nv.ERR_NULL
+    assert nv._lib.nvfp4_rht16(P, P, nv.F32, 32, 32, 32, 2, 0, None) == nv.ERR_DTYPE
+    rec = nv.c_recipe(0, 1)
+    ctx = nv.c_linear_ctx(0, 0, 0, t, t, t, t, t, t)
+    assert nv._lib.nvfp4_linear_fwd(P, P, P, 64, 64, 40, nv.BF16, ctypes.byref(rec),
+                                    ctypes.byref(ctx), P, 256, None) == nv.ERR_SHAPE
+    assert nv._lib.nvfp4_linear_fwd(P, P, P, 64, 64, 64, nv.BF16, None, ctypes.byref(ctx), P, 256,
+                                    None) == nv.ERR_NULL
+    # backward before a training forward on this ctx
+    assert nv._lib.nvfp4_linear_bwd(P, nv.BF16, ctypes.byref(ctx), P, P, nv.F32, 1,
+                                    ctypes.byref(rec), P, 256, None) == nv.ERR_SHAPE

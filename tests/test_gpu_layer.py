@@ -1,0 +1,74 @@
+"""GPU parity of the layer entry points nvfp4_linear_fwd / nvfp4_linear_bwd:
+every quantised operand in the context bit-exact against the oracle's layer
+composition, and the three GEMM outputs within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from tests.gpu_util import assert_gemm_close, assert_q_equal, np32, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import bit_quantized_numerics_amd as nv
+    return nv
+
+
+def _run_layer(nv, M, K, N, seed_base=0):
+    x = W.activations(M, K, seed=W.SEED_X + seed_base)
+    w = W.weights(N, K, seed=W.SEED_W + seed_base)
+    dy = W.gradients(M, N, seed=W.SEED_DY + seed_base)
+    signs = nv.nvfp4_rht_signs_from_seed(W.RHT_SEED)
+    ws = nv.Workspace("cuda")
+    nv.nvfp4_workspace_init(ws)
+    ctx = nv.LinearContext(M, K, N, "cuda")
+    say("layer", M, K, N)
+    y = nv.nvfp4_linear_fwd(x.cuda(), w.cuda(), ctx, ws, signs, training=True)
+    dx, dw = nv.nvfp4_linear_bwd(dy.cuda(), ctx, ws, signs, W.SR_SEED)
+    torch.cuda.synchronize()
+    assert nv.nvfp4_device_status(ws) == nv.OK
+    ops = O.linear_operands(np32(x), np32(w), np32(dy), O.Recipe(rht_signs=signs, sr_seed=W.SR_SEED))
+    for name in ("xq", "wq", "wqt", "xqt", "dyq", "dyqt"):
+        assert_q_equal(getattr(ctx, name), ops[name], name)
+    return ctx, ops, y, dx, dw, (x, w, dy)
+
+
+def test_layer_small(nv):
+    M, K, N = 256, 384, 512
+    ctx, ops, y, dx, dw, _ = _run_layer(nv, M, K, N, seed_base=10)
+    for out, (a, b), bf16, what in ((y, ("xq", "wq"), True, "Y"), (dx, ("dyq", "wqt"), True, "dX"),
+                                    (dw, ("dyqt", "xqt"), False, "dW")):
+        C, S = O.gemm(ops[a], ops[b])
+        assert_gemm_close(out.float().cpu().numpy(), C, S, bf16, what)
+
+
+def test_layer_dw_tracks_unquantised_gradient(nv):
+    """The RHT cancels in dY^T X (it is orthogonal along tokens), so the NVFP4
+    Wgrad stays close to the float64 dY^T X."""
+    M, K, N = 512, 256, 384
+    ctx, ops, y, dx, dw, (x, w, dy) = _run_layer(nv, M, K, N, seed_base=20)
+    ref = np32(dy).astype(np.float64).T @ np32(x).astype(np.float64)
+    rel = np.linalg.norm(dw.cpu().numpy() - ref) / np.linalg.norm(ref)
+    assert rel < 0.2
+
+
+@pytest.mark.slow
+def test_layer_full_size_sampled(nv):
+    """The benchmarked workload: 8192 tokens, 5120 -> 20480."""
+    M, K, N = W.LAYER_M, W.LAYER_K, W.LAYER_N
+    ctx, ops, y, dx, dw, _ = _run_layer(nv, M, K, N)
+    g = np.random.default_rng(5)
+    for out, (a, b), bf16, what in ((y, ("xq", "wq"), True, "Y"), (dx, ("dyq", "wqt"), True, "dX"),
+                                    (dw, ("dyqt", "xqt"), False, "dW")):
+        ra, rb = ops[a], ops[b]
+        ms = g.integers(0, ra.rows, 256)
+        ns = g.integers(0, rb.rows, 256)
+        um, im = np.unique(ms, return_inverse=True)
+        un, in_ = np.unique(ns, return_inverse=True)
+        Cs, Ss = O.gemm_entries(O.dequant_rows(ra, um), O.dequant_rows(rb, un), im, in_)
+        got = out[torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()].float().cpu().numpy()
+        assert_gemm_close(got, Cs, Ss, bf16, what)
