@@ -114,7 +114,8 @@ nvfp4_status check_gemm_operand(const nvfp4_tensor* t) {
   if (t->rows <= 0 || t->cols <= 0 || t->cols % 16 != 0) return NVFP4_ERR_SHAPE;
   if (t->scale_mode != NVFP4_SCALE_1X16 && t->scale_mode != NVFP4_SCALE_16X16) return NVFP4_ERR_DTYPE;
   if (t->scale_mode == NVFP4_SCALE_16X16 && t->rows % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (!aligned(t->codes, 16) || !aligned(t->global_scale, 4)) return NVFP4_ERR_ALIGN;
+  if (!aligned(t->codes, 16) || !aligned(t->scales, 4) || !aligned(t->global_scale, 4))
+    return NVFP4_ERR_ALIGN;
   return NVFP4_OK;
 }
 
@@ -322,7 +323,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, i
   if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (a->cols != b->cols) return NVFP4_ERR_SHAPE;
   if (ldc < b->rows) return NVFP4_ERR_SHAPE;
-  if (a->rows > (int64_t)65535 * 128) return NVFP4_ERR_SHAPE;
+  if ((a->rows + 255) / 256 * ((b->rows + 255) / 256) > (int64_t)0x7FFFFFFF) return NVFP4_ERR_SHAPE;
   if (!aligned(c, 4)) return NVFP4_ERR_ALIGN;
   NVFP4_HIP(launch_gemm(gemm_operand(a), gemm_operand(b), a->cols, c, c_dtype, ldc, as_stream(stream)));
   return NVFP4_OK;

@@ -37,7 +37,8 @@
  *     share a workspace must be issued on one stream (they reuse its slots).
  *   - Shapes: rows and cols are multiples of 16 except where stated; leading
  *     dimensions are in elements and >= cols; device pointers must be 16-byte
- *     aligned and ld * element size a multiple of 16 bytes.
+ *     aligned and ld * element size a multiple of 16 bytes; a GEMM operand's
+ *     scales pointer must be 4-byte aligned.
  */
 #ifndef NVFP4_H_
 #define NVFP4_H_
@@ -103,7 +104,8 @@ typedef struct {
 
 /* The pages' layer recipe [Review "Core idea" items (2)-(4); Captions
  * Fig. 5]: 16x16 weight scales, RHT on the Wgrad inputs only, stochastic
- * rounding on the gradient copies only.  Defaults via nvfp4_recipe_default. */
+ * rounding on the gradient copies only.  The pages fix one sign seed for the
+ * whole run: use nvfp4_rht_signs_from_seed(0) unless another is wanted. */
 typedef struct {
   uint32_t rht_signs;   /* sign diagonal shared by every RHT of the layer */
   int32_t training;     /* forward also builds the Wgrad copy of X */
