@@ -15,9 +15,12 @@ namespace {
 
 using namespace nvfp4;
 
-// Workspace: 64 uint32 words.  Word 0 is the sticky device status; the others
-// are amax slots (bit patterns of non-negative floats, reduced with atomicMax).
-constexpr size_t kWorkspaceBytes = 256;
+// Workspace: 8 regions of kAmaxRegionWords words (4 KB).  Word 0 of region 0
+// is the sticky device status; each other region holds the slots of one
+// tensor amax (bit patterns of non-negative floats, reduced with atomicMax,
+// kAmaxSlots words on separate 128-byte lines).
+constexpr int kRegions = 8;
+constexpr size_t kWorkspaceBytes = (size_t)kRegions * kAmaxRegionWords * 4;
 constexpr int kWsWords = (int)(kWorkspaceBytes / 4);
 enum Slot {
   kSlotStatus = 0,
@@ -31,7 +34,13 @@ enum Slot {
 };
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
-inline uint32_t* ws_word(void* ws, int slot) { return static_cast<uint32_t*>(ws) + slot; }
+inline uint32_t* ws_word(void* ws, int slot) {
+  return static_cast<uint32_t*>(ws) + (size_t)slot * kAmaxRegionWords;
+}
+// Zero `n` consecutive amax regions starting at `slot`.
+inline hipError_t zero_slots(void* ws, int slot, int n, hipStream_t s) {
+  return launch_zero_words(ws_word(ws, slot), n * kAmaxRegionWords, s);
+}
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t elem_bytes(int dtype) { return dtype == NVFP4_BF16 ? 2 : 4; }
 
@@ -224,7 +233,7 @@ nvfp4_status nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t 
     a.row = copy_args(out, workspace, slot, opts);
     flags = kFRow | (opts->round == NVFP4_SR ? kFSrRow : 0);
   }
-  NVFP4_HIP(launch_zero_words(ws_word(workspace, kSlotQRaw), 2, s));
+  NVFP4_HIP(zero_slots(workspace, kSlotQRaw, 2, s));
   NVFP4_HIP(launch_amax(x, dtype, rows, cols, ld, opts->rht_signs,
                         opts->rht ? nullptr : ws_word(workspace, kSlotQRaw),
                         opts->rht ? ws_word(workspace, kSlotQRht) : nullptr, s));
@@ -261,7 +270,7 @@ nvfp4_status nvfp4_quantize_rowcol(const void* x, int32_t dtype, int64_t rows, i
   const int flags = kFRow | kFCol | (opts_col->rht ? kFRht : 0) |
                     (opts_row->round == NVFP4_SR ? kFSrRow : 0) |
                     (opts_col->round == NVFP4_SR ? kFSrCol : 0);
-  NVFP4_HIP(launch_zero_words(ws_word(workspace, kSlotQRaw), 2, s));
+  NVFP4_HIP(zero_slots(workspace, kSlotQRaw, 2, s));
   NVFP4_HIP(launch_amax(x, dtype, rows, cols, ld, opts_col->rht_signs, ws_word(workspace, kSlotQRaw),
                         opts_col->rht ? ws_word(workspace, kSlotQRht) : nullptr, s));
   NVFP4_HIP(launch_quant_tile(dtype, flags, a, s));
@@ -291,7 +300,7 @@ nvfp4_status nvfp4_quantize_2d(const void* w, int32_t dtype, int64_t rows, int64
     a.col = copy_args(out_t, workspace, kSlotQRaw, nullptr);
     flags |= kFCol;
   }
-  NVFP4_HIP(launch_zero_words(ws_word(workspace, kSlotQRaw), 1, s));
+  NVFP4_HIP(zero_slots(workspace, kSlotQRaw, 1, s));
   NVFP4_HIP(launch_amax(w, dtype, rows, cols, ld, 0, ws_word(workspace, kSlotQRaw), nullptr, s));
   NVFP4_HIP(launch_quant_tile(dtype, flags, a, s));
   return NVFP4_OK;
@@ -350,7 +359,7 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
   set_shape(&ctx->xq, M, K, NVFP4_SCALE_1X16);
   set_shape(&ctx->wq, N, K, NVFP4_SCALE_16X16);
   set_shape(&ctx->wqt, K, N, NVFP4_SCALE_16X16);
-  NVFP4_HIP(launch_zero_words(ws_word(workspace, kSlotXRaw), 3, s));
+  NVFP4_HIP(zero_slots(workspace, kSlotXRaw, 3, s));
 
   // X: row-wise copy for Fprop and, when training, (R X)^T for Wgrad.
   TileArgs ax;
@@ -409,7 +418,7 @@ nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* c
   const hipStream_t s = as_stream(stream);
   set_shape(&ctx->dyq, M, N, NVFP4_SCALE_1X16);
   set_shape(&ctx->dyqt, N, M, NVFP4_SCALE_1X16);
-  NVFP4_HIP(launch_zero_words(ws_word(workspace, kSlotDyRaw), 2, s));
+  NVFP4_HIP(zero_slots(workspace, kSlotDyRaw, 2, s));
 
   // dY: SR row copy (stream 0) and SR (R dY)^T (stream 1) from one read.
   TileArgs ad;

@@ -134,26 +134,20 @@ __device__ __forceinline__ uint32_t fp4x8_rn(const float* v) {
   return w;
 }
 
-// Stochastic rounding of one scaled value v to an E2M1 code [Review s10 SR
-// formula; s7 SR example]: with lo <= |v| < hi the neighbouring grid values,
-// round up iff r16 < (|v| - lo)/(hi - lo) * 65536.  For |v| in [1, 6) the
-// fraction is exactly the fp32 mantissa bits below the E2M1 mantissa bit,
-// so the test is an integer compare.
-__device__ __forceinline__ uint32_t fp4_sr(float v, uint32_t r16) {
-  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
-  const float m = __builtin_fabsf(v);
-  uint32_t idx;
-  if (m >= 6.0f) {
-    idx = 7u;
-  } else if (m >= 1.0f) {
-    const uint32_t bits = __float_as_uint(m);
-    idx = (bits >> 22) - 252u + ((r16 << 6) < (bits & 0x3FFFFFu) ? 1u : 0u);
-  } else {
-    const uint32_t lo = m >= 0.5f ? 1u : 0u;
-    const float frac = (m - (lo ? 0.5f : 0.0f)) * 2.0f;
-    idx = lo + ((float)r16 < frac * 65536.0f ? 1u : 0u);
-  }
-  return sign | idx;
+// Stochastic rounding to E2M1 [Review s10 SR formula; s7 SR example]: with
+// lo <= |v| < hi the neighbouring grid values and T = floor((|v| - lo) /
+// (hi - lo) * 2^22) (the fraction in 22-bit fixed point), round up iff
+// 64 * r16 < T; |v| >= 6 gives 6.  gfx950's stochastic FP4 convert (first
+// element of the pair, unit scale) rounds up iff (rnd >> 10) + T >= 2^22
+// (established by an on-GPU sweep of its rounding), so rnd = ~(r16 << 16),
+// whose top 22 bits are 2^22 - 1 - 64 * r16, reproduces the rule exactly.
+// The code comes back in the low nibble of byte 0 (the compiler does not
+// keep the other bytes of the destination for this instruction, so results
+// are assembled with shifts instead of the byte-select operand).
+__device__ __forceinline__ uint32_t fp4_sr_hw(float v, uint32_t rnd) {
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  const float2_t pair = {v, 0.0f};
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, rnd, 1.0f, 0) & 0xFu;
 }
 
 // ---------------------------------------------------------------- Philox
@@ -188,14 +182,15 @@ __device__ __forceinline__ U4 sr_draw8(uint64_t seed, uint32_t stream, uint64_t 
                        (uint32_t)(seed >> 32));
 }
 
-// Eight values -> eight SR codes using the eight draws in r.
+// Eight values -> eight SR codes (value i in nibble i) using the eight 16-bit
+// draws in r (draw i = half i of the 128-bit output, low half first).
 __device__ __forceinline__ uint32_t fp4x8_sr(const float* v, const U4& r) {
-  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  const uint32_t w[4] = {~r.x, ~r.y, ~r.z, ~r.w};
   uint32_t out = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t r16 = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-    out |= fp4_sr(v[i], r16) << (4 * i);
+  for (int k = 0; k < 4; ++k) {
+    out |= fp4_sr_hw(v[2 * k], (w[k] << 16) | 0xFFFFu) << (8 * k);
+    out |= fp4_sr_hw(v[2 * k + 1], w[k] | 0xFFFFu) << (8 * k + 4);
   }
   return out;
 }

@@ -17,11 +17,17 @@ constexpr int kFRht = 8;     // RHT16 along rows before the column copy
 constexpr int kFSrRow = 16;  // stochastic rounding for the row copy
 constexpr int kFSrCol = 32;  // stochastic rounding for the column copy
 
+// A tensor amax lives in kAmaxSlots words kAmaxStride words apart (each on
+// its own 128-byte line); its value is the max over the slots.
+constexpr int kAmaxSlots = 32;
+constexpr int kAmaxStride = 32;
+constexpr int kAmaxRegionWords = kAmaxSlots * kAmaxStride;  // 4 KB
+
 struct CopyArgs {
   uint8_t* codes = nullptr;
   uint8_t* scales = nullptr;
   float* global = nullptr;
-  const uint32_t* amax = nullptr;  // device word holding the copy's amax bits
+  const uint32_t* amax = nullptr;  // the copy's amax slots (kAmaxSlots words)
   uint64_t seed = 0;
   uint64_t offset = 0;
   uint32_t stream = 0;

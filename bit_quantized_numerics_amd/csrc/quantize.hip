@@ -5,8 +5,10 @@
 // by numbered section; [Captions] = that paper's figure-caption list.
 //
 // Work decomposition.  Every kernel walks the source matrix x [rows, cols]
-// (row-major, cols contiguous) in tiles of 256 rows x 128 columns; each of
-// the 256 threads of a workgroup owns one 16-row x 8-column patch.  That
+// (row-major, cols contiguous) in tiles of 256 rows x 256 columns; each of
+// the 512 threads of a workgroup owns one 16-row x 8-column patch (32 patch
+// columns x 16 patch rows, so a wave covers two 16-row strips of 512 bytes
+// per row).  That
 // patch shape serves every block geometry of the layer:
 //   - a 1x16 block along cols is one row of the patch plus the neighbouring
 //     lane's row (lane ^ 1 holds the other 8 columns);
@@ -14,16 +16,26 @@
 //     [Review s2]) is one column of the patch, which is also exactly one
 //     16-token chunk of the random Hadamard transform [Review s3];
 //   - a 16x16 weight tile is the patch plus its neighbour lane's patch.
-// Reads are 16-byte loads, 16 per thread in flight; the column-wise copy is
-// staged in LDS so that each output row segment is written contiguously.
+// Reads are 16-byte loads, 16 per thread in flight.  Every row of the row-wise
+// copy is written as 128 contiguous bytes per tile.  Each 16-element column
+// block of the column-wise copy is one 8-byte store; the 16 row strips of a
+// workgroup fill each 128-byte output line within the same workgroup, so the
+// L2 merges them (an LDS transpose stage only added bank-conflicted stores).
+//
+// Tensor amax.  Each stats workgroup reduces its tile in LDS and adds one
+// atomicMax to one of kAmaxSlots words (chosen by workgroup id, each slot on
+// its own 128-byte line); consumers take the max of the slots.  A single
+// shared word would serialise thousands of device-scope atomics.
 #include "device_common.h"
 #include "internal.h"
 
 namespace nvfp4 {
 
 constexpr int kTileR = 256;  // source rows per workgroup
-constexpr int kTileC = 128;  // source cols per workgroup
-constexpr int kThreads = 256;
+constexpr int kTileC = 256;  // source cols per workgroup
+constexpr int kThreads = 512;
+constexpr int kStatsTileR = 128;  // stats kernel: 128 rows x 256 cols, 256 threads
+constexpr int kStatsThreads = 256;
 
 // ---------------------------------------------------------------- zero
 
@@ -60,11 +72,12 @@ __device__ __forceinline__ void load_patch(const TIn* x, int64_t rows, int64_t l
 // scale after the transform).
 
 template <typename TIn, bool RAW, bool RHTC>
-__global__ __launch_bounds__(kThreads) void amax_kernel(const TIn* __restrict__ x, int64_t rows,
-                                                        int64_t cols, int64_t ld, uint32_t signs,
-                                                        uint32_t* out_raw, uint32_t* out_rht) {
-  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
-  const int64_t r0 = (int64_t)blockIdx.y * kTileR + rs * 16;
+__global__ __launch_bounds__(kStatsThreads) void amax_kernel(const TIn* __restrict__ x,
+                                                             int64_t rows, int64_t cols, int64_t ld,
+                                                             uint32_t signs, uint32_t* out_raw,
+                                                             uint32_t* out_rht) {
+  const int t = threadIdx.x, cg = t & 31, rs = t >> 5;
+  const int64_t r0 = (int64_t)blockIdx.y * kStatsTileR + rs * 16;
   const int64_t c0 = (int64_t)blockIdx.x * kTileC + cg * 8;
   const bool valid = r0 < rows && c0 < cols;
   float v[16][8];
@@ -90,11 +103,24 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const TIn* __restrict__ 
         m_rht = m_rht > b ? m_rht : b;
       }
   }
+  __shared__ uint32_t red[2][kStatsThreads / 64];
   if (RAW) m_raw = wave_max_u32(m_raw);
   if (RHTC) m_rht = wave_max_u32(m_rht);
   if ((t & 63) == 0) {
-    if (RAW) atomicMax(out_raw, m_raw);
-    if (RHTC) atomicMax(out_rht, m_rht);
+    red[0][t >> 6] = m_raw;
+    red[1][t >> 6] = m_rht;
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint32_t r0 = 0, r1 = 0;
+#pragma unroll
+    for (int w = 0; w < kStatsThreads / 64; ++w) {
+      r0 = r0 > red[0][w] ? r0 : red[0][w];
+      r1 = r1 > red[1][w] ? r1 : red[1][w];
+    }
+    const int slot = (int)((blockIdx.x + blockIdx.y * 7u) % kAmaxSlots) * kAmaxStride;
+    if (RAW) atomicMax(out_raw + slot, r0);
+    if (RHTC) atomicMax(out_rht + slot, r1);
   }
 }
 
@@ -102,17 +128,18 @@ template <typename TIn>
 static hipError_t amax_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ld,
                                 uint32_t signs, uint32_t* out_raw, uint32_t* out_rht,
                                 hipStream_t s) {
-  const dim3 grid((unsigned)((cols + kTileC - 1) / kTileC), (unsigned)((rows + kTileR - 1) / kTileR));
+  const dim3 grid((unsigned)((cols + kTileC - 1) / kTileC),
+                  (unsigned)((rows + kStatsTileR - 1) / kStatsTileR));
   const TIn* p = static_cast<const TIn*>(x);
   if (out_raw && out_rht)
-    hipLaunchKernelGGL((amax_kernel<TIn, true, true>), grid, dim3(kThreads), 0, s, p, rows, cols, ld,
-                       signs, out_raw, out_rht);
+    hipLaunchKernelGGL((amax_kernel<TIn, true, true>), grid, dim3(kStatsThreads), 0, s, p, rows, cols,
+                       ld, signs, out_raw, out_rht);
   else if (out_raw)
-    hipLaunchKernelGGL((amax_kernel<TIn, true, false>), grid, dim3(kThreads), 0, s, p, rows, cols,
-                       ld, signs, out_raw, out_rht);
+    hipLaunchKernelGGL((amax_kernel<TIn, true, false>), grid, dim3(kStatsThreads), 0, s, p, rows,
+                       cols, ld, signs, out_raw, out_rht);
   else
-    hipLaunchKernelGGL((amax_kernel<TIn, false, true>), grid, dim3(kThreads), 0, s, p, rows, cols,
-                       ld, signs, out_raw, out_rht);
+    hipLaunchKernelGGL((amax_kernel<TIn, false, true>), grid, dim3(kStatsThreads), 0, s, p, rows,
+                       cols, ld, signs, out_raw, out_rht);
   return hipGetLastError();
 }
 
@@ -128,7 +155,8 @@ hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int
 // the amax is not finite (that copy is then skipped).
 __device__ __forceinline__ bool copy_scales(const uint32_t* amax, uint32_t* status,
                                             TensorScales* ts) {
-  const uint32_t bits = *amax;
+  const int lane = threadIdx.x & 63;
+  const uint32_t bits = wave_max_u32(lane < kAmaxSlots ? amax[lane * kAmaxStride] : 0u);
   if (bits >= kInfBits) {
     if (threadIdx.x == 0) atomicMax(status, kStatusNonfinite);
     return false;
@@ -141,11 +169,8 @@ template <typename TIn, int F>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
   constexpr bool ROW = F & kFRow, COL = F & kFCol, TWO_D = F & kF2D, RHT = F & kFRht;
   constexpr bool SR_ROW = F & kFSrRow, SR_COL = F & kFSrCol;
-  constexpr int kPitch = kTileR / 2 + 8;  // LDS row pitch (bytes) of the staged column copy
-  __shared__ __align__(16) uint8_t lds_codes[COL ? kTileC : 1][COL ? kPitch : 8];
-  __shared__ uint8_t lds_scales[(COL && !TWO_D) ? kTileC : 1][kTileR / 16];
 
-  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
+  const int t = threadIdx.x, cg = t & 31, rs = t >> 5;
   const int64_t rows = a.rows, cols = a.cols;
   const int64_t tile_r0 = (int64_t)blockIdx.y * kTileR, tile_c0 = (int64_t)blockIdx.x * kTileC;
   const int64_t r0 = tile_r0 + rs * 16, c0 = tile_c0 + cg * 8;
@@ -203,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
           uint2 w;
           w.x = fp4x8_rn(s);
           w.y = fp4x8_rn(s + 8);
-          *reinterpret_cast<uint2*>(&lds_codes[cg * 8 + j][rs * 8]) = w;
+          *reinterpret_cast<uint2*>(a.col.codes + (c0 + j) * (rows / 2) + r0 / 2) = w;
         }
       }
     }
@@ -255,36 +280,14 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
           w.x = fp4x8_rn(s);
           w.y = fp4x8_rn(s + 8);
         }
-        *reinterpret_cast<uint2*>(&lds_codes[cg * 8 + j][rs * 8]) = w;
-        lds_scales[cg * 8 + j][rs] = (uint8_t)dcode;
-      }
-    }
-  }
-
-  if (COL) {
-    __syncthreads();
-    if (do_col) {
-      // operand = x^T: row gr (a source column) holds rows/2 code bytes
-      const int64_t pitch = rows / 2;
-#pragma unroll
-      for (int q = t; q < kTileC * 16; q += kThreads) {
-        const int orow = q >> 4, p = q & 15;
-        const int64_t gr = tile_c0 + orow, ge = tile_r0 + p * 16;
-        if (gr < cols && ge < rows)
-          *reinterpret_cast<uint2*>(a.col.codes + gr * pitch + ge / 2) =
-              *reinterpret_cast<const uint2*>(&lds_codes[orow][p * 8]);
-      }
-      if (!TWO_D) {
-        const int64_t spitch = rows / 16;
-#pragma unroll
-        for (int q = t; q < kTileC * 16; q += kThreads) {
-          const int orow = q >> 4, p = q & 15;
-          const int64_t gr = tile_c0 + orow, ge = tile_r0 + p * 16;
-          if (gr < cols && ge < rows) a.col.scales[gr * spitch + ge / 16] = lds_scales[orow][p];
+        if (valid) {
+          *reinterpret_cast<uint2*>(a.col.codes + (c0 + j) * (rows / 2) + r0 / 2) = w;
+          a.col.scales[(c0 + j) * (rows / 16) + r0 / 16] = (uint8_t)dcode;
         }
       }
     }
   }
+
 }
 
 template <typename TIn, int F>
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void rht16_axis0_kernel(const TIn* __rest
                                                                float* __restrict__ y, int64_t rows,
                                                                int64_t cols, int64_t ld,
                                                                uint32_t signs) {
-  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
+  const int t = threadIdx.x, cg = t & 31, rs = t >> 5;
   const int64_t r0 = (int64_t)blockIdx.y * kTileR + rs * 16;
   const int64_t c0 = (int64_t)blockIdx.x * kTileC + cg * 8;
   const bool valid = r0 < rows && c0 < cols;

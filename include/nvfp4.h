@@ -131,7 +131,7 @@ typedef struct {
 nvfp4_status nvfp4_tensor_bytes(int64_t rows, int64_t cols, int32_t scale_mode,
                                 size_t* codes_bytes, size_t* scales_bytes);
 
-/* Minimum workspace size in bytes (a small constant). */
+/* Minimum workspace size in bytes (a constant, 32 KB). */
 size_t nvfp4_workspace_bytes(void);
 
 /* Host-side: the sign diagonal from a seed = low 16 bits of word 0 of

@@ -68,8 +68,11 @@ int oracle_e2m1_rn_index(float m) {
 /* Stochastic rounding of a non-negative magnitude [Review s10 SR formula and
  * s7 SR mini-example]: with lo <= m < hi the neighbouring grid values, the
  * result is hi with probability (m-lo)/(hi-lo), else lo.  The random source
- * is a 16-bit integer r16, uniform on [0, 65536): round up iff
- * r16 < (m-lo)/(hi-lo) * 65536.  Magnitudes at or beyond 6 give 6. */
+ * is a 16-bit integer r16, uniform on [0, 65536), and the fraction is taken
+ * in 22-bit fixed point (exactly the fp32 mantissa bits below the E2M1
+ * mantissa bit when m >= 1, truncated below that): with
+ * T = floor((m-lo)/(hi-lo) * 2^22), round up iff 64 * r16 < T.  Magnitudes at
+ * or beyond 6 give 6. */
 int oracle_e2m1_sr_index(float m, uint32_t r16) {
   if (m >= 6.0f) return 7;
   int lo = 0;
@@ -78,8 +81,8 @@ int oracle_e2m1_sr_index(float m, uint32_t r16) {
   float lo_v = (float)kE2M1[lo];
   float hi_v = (float)kE2M1[lo + 1];
   float frac = (m - lo_v) / (hi_v - lo_v);
-  float thresh = frac * 65536.0f;
-  return ((float)r16 < thresh) ? lo + 1 : lo;
+  double T = floor((double)frac * 4194304.0);
+  return (64.0 * (double)r16 < T) ? lo + 1 : lo;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -55,11 +55,13 @@ def nearest_even(value: Fraction, table) -> int:
 
 
 def sr_index(m: Fraction, r16: int) -> int:
+    """Round up iff 64 * r16 < floor(frac * 2^22) (fraction in 22-bit fixed point)."""
     if m >= E2M1[-1]:
         return 7
     lo = max(i for i, t in enumerate(E2M1) if t <= m)
     frac = (m - E2M1[lo]) / (E2M1[lo + 1] - E2M1[lo])
-    return lo + 1 if r16 < frac * 65536 else lo
+    T = (frac * 2**22).numerator // (frac * 2**22).denominator
+    return lo + 1 if 64 * r16 < T else lo
 
 
 # ---------------------------------------------------------------- Philox4x32-10

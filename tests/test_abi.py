@@ -37,7 +37,7 @@ def test_tensor_bytes():
 
 
 def test_workspace_bytes_and_status_strings():
-    assert nv.nvfp4_workspace_bytes() >= 64
+    assert nv.nvfp4_workspace_bytes() >= 4096
     for s in range(8):
         assert nv.nvfp4_status_string(s)
 
@@ -56,7 +56,10 @@ def _tensor(codes=P, scales=P, glob=P):
     return nv.c_tensor(codes, scales, glob, 0, 0, 0)
 
 
-def _q(x=P, dtype=nv.BF16, rows=64, cols=256, ld=256, opts=None, out=None, ws=P, wsb=256):
+WSB = nv.nvfp4_workspace_bytes()
+
+
+def _q(x=P, dtype=nv.BF16, rows=64, cols=256, ld=256, opts=None, out=None, ws=P, wsb=WSB):
     o = opts or nv.c_quant_opts(0, 0, 0, 0, 0, 0, 0)
     t = out or _tensor()
     return nv._lib.nvfp4_quantize(x, dtype, rows, cols, ld, ctypes.byref(o), ctypes.byref(t), ws,
@@ -74,7 +77,7 @@ def test_quantize_argument_errors():
     assert _q(ld=260) == nv.ERR_ALIGN
     assert _q(out=_tensor(codes=P + 4)) == nv.ERR_ALIGN
     assert _q(ws=None) == nv.ERR_WORKSPACE
-    assert _q(wsb=16) == nv.ERR_WORKSPACE
+    assert _q(wsb=WSB - 4) == nv.ERR_WORKSPACE
     assert _q(opts=nv.c_quant_opts(2, 0, 0, 0, 0, 0, 0)) == nv.ERR_DTYPE
     assert _q(opts=nv.c_quant_opts(1, 0, 0, 0, 0, 8, 0)) == nv.ERR_ALIGN       # offset % 16
     assert _q(opts=nv.c_quant_opts(0, 0, 1, 0, 0, 0, 0)) == nv.ERR_SHAPE       # RHT needs transpose
@@ -99,7 +102,7 @@ def test_gemm_argument_errors():
 
 def test_2d_rht_and_layer_argument_errors():
     t = _tensor()
-    assert nv._lib.nvfp4_quantize_2d(P, nv.BF16, 40, 32, 32, ctypes.byref(t), None, P, 256,
+    assert nv._lib.nvfp4_quantize_2d(P, nv.BF16, 40, 32, 32, ctypes.byref(t), None, P, WSB,
                                      None) == nv.ERR_SHAPE
     assert nv._lib.nvfp4_rht16(P, P, nv.F32, 24, 32, 32, 0, 0, None) == nv.ERR_SHAPE
     assert nv._lib.nvfp4_rht16(P, P, nv.F32, 32, 24, 24, 1, 0, None) == nv.ERR_SHAPE
@@ -108,9 +111,9 @@ def test_2d_rht_and_layer_argument_errors():
     rec = nv.c_recipe(0, 1)
     ctx = nv.c_linear_ctx(0, 0, 0, t, t, t, t, t, t)
     assert nv._lib.nvfp4_linear_fwd(P, P, P, 64, 64, 40, nv.BF16, ctypes.byref(rec),
-                                    ctypes.byref(ctx), P, 256, None) == nv.ERR_SHAPE
-    assert nv._lib.nvfp4_linear_fwd(P, P, P, 64, 64, 64, nv.BF16, None, ctypes.byref(ctx), P, 256,
+                                    ctypes.byref(ctx), P, WSB, None) == nv.ERR_SHAPE
+    assert nv._lib.nvfp4_linear_fwd(P, P, P, 64, 64, 64, nv.BF16, None, ctypes.byref(ctx), P, WSB,
                                     None) == nv.ERR_NULL
     # backward before a training forward on this ctx
     assert nv._lib.nvfp4_linear_bwd(P, nv.BF16, ctypes.byref(ctx), P, P, nv.F32, 1,
-                                    ctypes.byref(rec), P, 256, None) == nv.ERR_SHAPE
+                                    ctypes.byref(rec), P, WSB, None) == nv.ERR_SHAPE

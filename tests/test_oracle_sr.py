@@ -48,10 +48,12 @@ def _count_up(m):
     return idx
 
 
-@pytest.mark.parametrize("m", [0.1, 0.26, 0.5, 0.74, 1.03, 1.2499, 1.6, 2.2, 2.9999, 3.5, 4.7, 5.99])
+@pytest.mark.parametrize("m", [0.1, 0.26, 0.5, 0.74, 1.03, 1.2499, 1.6, 2.2, 2.9999, 3.5, 4.7, 5.99,
+                               3e-4, 1.7e-6, 2.0 ** -30])
 def test_sr_exact_enumeration(m):
     """Over all 2^16 values of the 16-bit draw the round-up count equals
-    ceil(frac * 2^16) with frac = (m - lo)/(hi - lo) computed exactly."""
+    ceil(T / 64) with T = floor(frac * 2^22), frac = (m - lo)/(hi - lo)
+    computed exactly: probability T / 2^22 to within one 2^-16 step."""
     from fractions import Fraction
     m32 = np.float32(m)
     idx = _count_up(m32)
@@ -59,10 +61,25 @@ def test_sr_exact_enumeration(m):
     mf = Fraction(float(m32))
     lo = max(i for i, t in enumerate(tv) if t <= mf)
     frac = (mf - tv[lo]) / (tv[lo + 1] - tv[lo])
+    T = int(frac * 2**22)  # floor (frac >= 0)
     n_up = int((idx == lo + 1).sum())
     assert set(np.unique(idx)) <= {lo, lo + 1}
-    want = -((-frac * 65536).numerator // (frac * 65536).denominator)  # ceil
-    assert n_up == want
+    assert n_up == -(-T // 64)
+    assert abs(n_up / 65536 - float(frac)) <= 2.0 ** -16
+
+
+def test_sr_22bit_fraction_boundaries():
+    """The fraction is kept to 22 bits: for |v| >= 1 that is every mantissa
+    bit below the E2M1 bit (no truncation); below 1 the lower bits drop."""
+    # 1 + 64*k * 2^-23 has T = 64k: draw r16 = k is the first not rounding up
+    for k in (1, 7, 1000):
+        m = np.float32(1.0 + 64 * k * 2.0 ** -22 / 2)
+        assert O.e2m1_sr_index(m, k - 1) == 3 and O.e2m1_sr_index(m, k) == 2
+    # a magnitude whose fraction has bits only below 2^-22 never rounds up
+    assert O.e2m1_sr_index(np.float32(2.0 ** -30), 0) == 0
+    # just above a multiple of 64 / 2^22 in the subnormal range: truncated to it
+    m = np.float32((64 * 3 + 0.5) * 2.0 ** -23)   # frac * 2^22 = 192.5 -> T = 192
+    assert O.e2m1_sr_index(m, 2) == 1 and O.e2m1_sr_index(m, 3) == 0
 
 
 def test_sr_page_mini_example():
