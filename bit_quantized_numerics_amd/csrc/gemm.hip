@@ -21,14 +21,26 @@
 //
 // Structure.  A workgroup of 4 waves computes a 256 x 256 tile of C; each
 // wave owns 128 x 128 (4 x 4 MFMA blocks of 32 x 32; 256 FP32 accumulators
-// per lane, held in AGPRs).  There is no LDS stage and no barrier: each wave
-// loads the NVFP4 codes of its own 4 A and 4 B 32-row blocks straight from
-// global memory (L1/L2 absorb the sharing between the two waves that read the
-// same rows) into registers, three K-steps ahead, and dequantises them one
-// MFMA sub-step ahead, so that on gfx950 -- where a 16-byte LDS store runs at
-// well under half the rate of a load and the fp4->f16 convert costs two issue
-// passes -- the only per-element work left is 2 VALU instructions per pair of
-// elements, about 4 per MFMA, issued in the MFMA's shadow.
+// per lane, held in AGPRs).  Per MFMA the wave dequantises a quarter of one
+// row block of the next sub-step (4 VALU instructions: two converts, two
+// scale multiplies), written in issue order with a scheduling fence after
+// every MFMA so that the VALU work and the loads sit evenly in the MFMA
+// shadow.  Two kernels share that inner loop and differ in how the NVFP4
+// codes reach the registers:
+//
+//  * gemm_lds_kernel (K % 128 == 0, K >= 384; the training shapes): the codes
+//    and scales of a 128-wide K slab of both 256-row operand tiles are copied
+//    straight from global memory into LDS by buffer loads in LDS mode (no VGPR
+//    staging; each group of 4 lanes reads one row's 64 bytes, so every load
+//    moves whole cache lines), with up to three slabs in flight in four LDS
+//    buffers (144 KB).  Each wave then reads its fragments with one 16-byte
+//    LDS read per row block and K-step.  fp4 codes are a quarter of the f16
+//    bytes, so LDS carries ~16 B/clk per CU, far below its rate.  Rows past
+//    the operand fall outside the buffer's record count and load as zeros.
+//  * gemm_direct_kernel (any K % 16 == 0): each wave loads its own rows'
+//    codes straight from global memory into registers, two K-steps ahead,
+//    with the two waves that share rows meeting in L1.  Each load instruction
+//    touches one line per row, so this is the fallback for other shapes.
 //
 // K order inside a step.  A K-step covers 64 k.  For MFMA sub-step s (0..3)
 // lane-half h (lanes 32h..32h+31) supplies k = 32h + 8s + (0..7) instead of
@@ -54,6 +66,8 @@ constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8;  // tile-row group for L2 reuse
 
+// ------------------------------------------------------------ inner loop
+
 // The codes and scales one lane needs for one K-step: for each of its 4 A and
 // 4 B 32-row blocks, 32 codes (16 bytes: k = 32h .. 32h+31 of the step) and
 // the row's four E4M3 scale bytes of the step (the lane uses bytes 2h, 2h+1).
@@ -61,6 +75,161 @@ struct StepRaw {
   uint4 ca[4], cb[4];
   uint32_t sa[4], sb[4];
 };
+
+// Fragments of one MFMA sub-step as packed half2 words: [block][pair], blocks
+// 0..3 the wave's A row blocks, 4..7 its B row blocks.
+typedef uint32_t Frags[8][4];
+
+__device__ __forceinline__ half8_t as_half8(const uint32_t (&w)[4]) {
+  half8_t h;
+  __builtin_memcpy(&h, w, 16);
+  return h;
+}
+
+// Word S (the codes of sub-step S) of block b of a K-step.
+__device__ __forceinline__ uint32_t word_of(const StepRaw& r, int b, int S) {
+  const uint4& v = b < 4 ? r.ca[b] : r.cb[b - 4];
+  return S == 0 ? v.x : S == 1 ? v.y : S == 2 ? v.z : v.w;
+}
+
+// Two of the four E4M3 scale bytes in s -> two fp16 values d * 2^-8 (bit
+// patterns code << 7), packed: the selector `sel` (per lane-half) places byte
+// 2h at bits 0..7 and byte 2h+1 at bits 16..23; the shift by 7 then cannot
+// carry across halves (codes are at most 0x7E).
+__device__ __forceinline__ uint32_t scale_pair(uint32_t s, uint32_t sel) {
+  return __builtin_amdgcn_perm(0u, s, sel) << 7;
+}
+
+// Codes 2p, 2p+1 of w times the fp16 scale in half `hi` of dpair.
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t w, uint32_t dpair, bool hi, int p) {
+  half2_t d2;
+  __builtin_memcpy(&d2, &dpair, 4);
+  const _Float16 d = hi ? d2[1] : d2[0];
+  const half2_t dd = {d, d};
+  half2_t c;
+  switch (p) {
+    case 0: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0); break;
+    case 1: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1); break;
+    case 2: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2); break;
+    default: c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3); break;
+  }
+  const half2_t v = c * dd;
+  uint32_t o;
+  __builtin_memcpy(&o, &v, 4);
+  return o;
+}
+
+// MFMA sub-step S of a K-step, written in issue order: chunk G issues MFMA
+// (G/4, G%4) on `src`, then dequantises a quarter of the next sub-step's
+// fragments into `dst` (pairs 2(G%2), 2(G%2)+1 of block G/2: sub-step S+1 of
+// `cur`, or, in sub-step 3, sub-step 0 of `nxt` after converting that block's
+// scales -- zero when `nxt_in_k` is false), and in sub-step 0 the memory
+// operation mem(G) (an LDS or global load of a later K-step).  A scheduling
+// fence after each chunk keeps this order.
+template <int S, class Mem>
+__device__ __forceinline__ void sub_step(float16_t (&acc)[4][4], const Frags& src, Frags& dst,
+                                         uint32_t (&dp)[8], const StepRaw& cur,
+                                         const StepRaw& nxt, bool nxt_in_k, uint32_t sel,
+                                         Mem& mem) {
+#pragma unroll
+  for (int G = 0; G < 16; ++G) {
+    const int i = G >> 2, j = G & 3, b = G >> 1, p0 = 2 * (G & 1);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(src[i]), as_half8(src[4 + j]),
+                                                       acc[i][j], 0, 0, 0);
+    if (S == 0) mem(G);
+    if (S < 3) {
+      const uint32_t w = word_of(cur, b, S + 1);
+      dst[b][p0] = dequant_pair(w, dp[b], S + 1 >= 2, p0);
+      dst[b][p0 + 1] = dequant_pair(w, dp[b], S + 1 >= 2, p0 + 1);
+    } else {
+      if ((G & 1) == 0)
+        dp[b] = nxt_in_k ? scale_pair(b < 4 ? nxt.sa[b] : nxt.sb[b - 4], sel) : 0u;
+      const uint32_t w = word_of(nxt, b, 0);
+      dst[b][p0] = dequant_pair(w, dp[b], false, p0);
+      dst[b][p0 + 1] = dequant_pair(w, dp[b], false, p0 + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One K-step of 64: on entry `f` holds sub-step 0 of `cur` and dp its scales;
+// on exit they hold sub-step 0 of `nxt`.  mem(0..15) runs during sub-step 0.
+template <class Mem>
+__device__ __forceinline__ void k_step(float16_t (&acc)[4][4], Frags& f, uint32_t (&dp)[8],
+                                       const StepRaw& cur, const StepRaw& nxt, bool nxt_in_k,
+                                       uint32_t sel, Mem& mem) {
+  Frags g;
+  sub_step<0>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem);
+  sub_step<1>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem);
+  sub_step<2>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem);
+  sub_step<3>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem);
+}
+
+// Sub-step 0 fragments and scales of the first K-step.
+__device__ __forceinline__ void first_frags(const StepRaw& r, uint32_t sel, Frags& f,
+                                            uint32_t (&dp)[8]) {
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    dp[b] = scale_pair(b < 4 ? r.sa[b] : r.sb[b - 4], sel);
+    const uint32_t w = word_of(r, b, 0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) f[b][p] = dequant_pair(w, dp[b], false, p);
+  }
+}
+
+// ------------------------------------------------------------ tiles, output
+
+// Workgroup -> output tile.  Workgroups are dispatched round-robin over the 8
+// XCDs; consecutive ids are first regrouped so that each XCD works on one
+// contiguous range, then ordered in groups of kGroupM tile rows so that the
+// tiles an XCD runs together share A and B rows in its L2.
+__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int* tm, int* tn) {
+  const int nwg = (int)gridDim.x;
+  int b = (int)blockIdx.x;
+  if ((nwg & 7) == 0) b = (b & 7) * (nwg >> 3) + (b >> 3);
+  const int per_group = kGroupM * tiles_n;
+  const int group = b / per_group;
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_group = b - group * per_group;
+  *tm = first_m + in_group % gsize;
+  *tn = in_group / gsize;
+}
+
+__device__ __forceinline__ void zero_acc(float16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+// Scaled accumulators -> C (bf16 nearest-even or fp32); rows and columns past
+// the operands are not stored.  (mw, nw) is the wave's first row and column.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_tile(const float16_t (&acc)[4][4], float gab, int64_t mw,
+                                           int64_t nw, int64_t rows_a, int64_t rows_b, int lane,
+                                           void* __restrict__ c, int64_t ldc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = mw + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t n = nw + j * 32 + (lane & 31);
+        if (m < rows_a && n < rows_b) {
+          const float v = acc[i][j][r] * gab;
+          if (OUT_BF16)
+            static_cast<uint16_t*>(c)[m * ldc + n] = f32_to_bf16_rne(v);
+          else
+            static_cast<float*>(c)[m * ldc + n] = v;
+        }
+      }
+}
+
+// ------------------------------------------------------------ direct kernel
 
 // Per-lane bases of one operand's 4 row blocks.
 struct OpBase {
@@ -81,166 +250,53 @@ __device__ __forceinline__ OpBase op_base(const GemmOperand& op, int64_t K, int6
 }
 
 // 16 code bytes + 4 scale bytes of one row block at step start k0 (the lane's
-// elements are k0 + 32h .. +31).  Rows past the operand read row 0 instead:
-// their products only reach rows or columns of C that are never stored.
-// Steps past K read step 0 instead; their scales are zeroed where they are
-// consumed (scales_of), which zeroes every dequantised value (E2M1 has no Inf
-// or NaN), so they add exact zeros.  Zeroing at load time would force a wait
-// for the load right after issuing it.
-template <bool K_ALIGNED>
+// elements are k0 + 32h .. +31; K a multiple of 16).  Rows past the operand
+// read row 0 instead: their products only reach rows or columns of C that are
+// never stored.  16-element blocks past K load zero codes and zero scales;
+// whole steps past K read step 0 instead and have their scales zeroed where
+// they are consumed (sub_step), which zeroes every dequantised value (E2M1
+// has no Inf or NaN), so they add exact zeros.
 __device__ __forceinline__ void load_blk(const OpBase& ob, int i, int64_t K, int64_t k0, int h,
                                          uint4& c, uint32_t& sc) {
-  if (K_ALIGNED) {  // K % 64 == 0: branch-free, the lane's 32 elements all exist
-    const int64_t kc = k0 < K ? k0 : 0;
-    c = *reinterpret_cast<const uint4*>(ob.codes[i] + kc / 2);
-    sc = *reinterpret_cast<const uint32_t*>(ob.scales[i] + kc / 16);
-    return;
-  }
-  c = make_uint4(0, 0, 0, 0);  // general K (multiple of 16): per 16-element block
+  const int64_t kb = k0 < K ? k0 : 0;
+  c = make_uint4(0, 0, 0, 0);
   sc = 0;
-  const int64_t kk = k0 + 32 * h;
+  const int64_t kk = kb + 32 * h;
   if (kk < K) {
-    const uint2 v = *reinterpret_cast<const uint2*>(ob.codes[i] + k0 / 2);
+    const uint2 v = *reinterpret_cast<const uint2*>(ob.codes[i] + kb / 2);
     c.x = v.x;
     c.y = v.y;
-    sc = (uint32_t)ob.scales[i][k0 / 16 + 2 * h] << (16 * h);
+    sc = (uint32_t)ob.scales[i][kb / 16 + 2 * h] << (16 * h);
   }
   if (kk + 16 < K) {
-    const uint2 v = *reinterpret_cast<const uint2*>(ob.codes[i] + k0 / 2 + 8);
+    const uint2 v = *reinterpret_cast<const uint2*>(ob.codes[i] + kb / 2 + 8);
     c.z = v.x;
     c.w = v.y;
-    sc |= (uint32_t)ob.scales[i][k0 / 16 + 2 * h + 1] << (16 * h + 8);
+    sc |= (uint32_t)ob.scales[i][kb / 16 + 2 * h + 1] << (16 * h + 8);
   }
 }
 
-template <bool K_ALIGNED>
-__device__ __forceinline__ void load_step(const OpBase& oa, const OpBase& obb, int64_t K, int64_t k0,
-                                          int h, StepRaw& r) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    load_blk<K_ALIGNED>(oa, i, K, k0, h, r.ca[i], r.sa[i]);
-    load_blk<K_ALIGNED>(obb, i, K, k0, h, r.cb[i], r.sb[i]);
+// Loads of K-step k0 into `fill`, one row block per chunk (chunks 0..7).
+struct DirectMem {
+  const OpBase& oa;
+  const OpBase& ob;
+  int64_t K, k0;
+  int h;
+  StepRaw& fill;
+  __device__ __forceinline__ void operator()(int G) {
+    if (G < 4)
+      load_blk(oa, G, K, k0, h, fill.ca[G], fill.sa[G]);
+    else if (G < 8)
+      load_blk(ob, G - 4, K, k0, h, fill.cb[G - 4], fill.sb[G - 4]);
   }
-}
+};
 
-// Two of the four E4M3 scale bytes in s -> two fp16 values d * 2^-8 (bit
-// patterns code << 7), packed: the selector `sel` (per lane-half) places byte
-// 2h at bits 0..7 and byte 2h+1 at bits 16..23; the shift by 7 then cannot
-// carry across halves (codes are at most 0x7E).
-__device__ __forceinline__ uint32_t scale_pair(uint32_t s, uint32_t sel) {
-  return __builtin_amdgcn_perm(0u, s, sel) << 7;
-}
-
-__device__ __forceinline__ half8_t dequant8(uint32_t w, uint32_t dpair, bool hi) {
-  half2_t d2;
-  __builtin_memcpy(&d2, &dpair, 4);
-  const _Float16 d = hi ? d2[1] : d2[0];
-  const half2_t dd = {d, d};
-  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * dd;
-  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * dd;
-  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * dd;
-  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * dd;
-  half8_t o = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-  return o;
-}
-
-// Sub-step S fragments (A and B) of a step; dp* are the converted scales.
-template <int S>
-__device__ __forceinline__ void dequant_sub(const StepRaw& r, const uint32_t (&dpa)[4],
-                                            const uint32_t (&dpb)[4], half8_t (&fa)[4],
-                                            half8_t (&fb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t wa = S == 0 ? r.ca[i].x : S == 1 ? r.ca[i].y : S == 2 ? r.ca[i].z : r.ca[i].w;
-    const uint32_t wb = S == 0 ? r.cb[i].x : S == 1 ? r.cb[i].y : S == 2 ? r.cb[i].z : r.cb[i].w;
-    fa[i] = dequant8(wa, dpa[i], S >= 2);
-    fb[i] = dequant8(wb, dpb[i], S >= 2);
-  }
-}
-
-// Converted scales of a step; `in_k` false (a step past K) gives zeros.
-__device__ __forceinline__ void scales_of(const StepRaw& r, bool in_k, uint32_t sel,
-                                          uint32_t (&dpa)[4], uint32_t (&dpb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    dpa[i] = in_k ? scale_pair(r.sa[i], sel) : 0u;
-    dpb[i] = in_k ? scale_pair(r.sb[i], sel) : 0u;
-  }
-}
-
-__device__ __forceinline__ void mfma16(float16_t (&acc)[4][4], const half8_t (&fa)[4],
-                                       const half8_t (&fb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-}
-
-// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedVmemRead = 0x020;
-
-// Interleave 16 MFMAs with VALU VALU instructions each and VMEM loads.
-template <int VALU, int VMEM>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int g = 0; g < 16; ++g) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU, 0);
-    if (g < VMEM) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-  }
-}
-
-// One K-step.  On entry `fa/fb` hold sub-step 0 of step k (from `cur`) and
-// `cdp*` its scales; `nxt` holds step k+1 (loaded earlier).  The loads of step
-// k+2 go into `fill`, issued during sub-step 0.  On exit fa/fb hold sub-step 0
-// of step k+1 and cdp* its scales.
-template <bool K_ALIGNED>
-__device__ __forceinline__ void k_step(float16_t (&acc)[4][4], half8_t (&fa)[4], half8_t (&fb)[4],
-                                       uint32_t (&cdpa)[4], uint32_t (&cdpb)[4], const StepRaw& cur,
-                                       const StepRaw& nxt, StepRaw& fill, const OpBase& oa,
-                                       const OpBase& ob, int64_t K, int64_t k_fill, int h,
-                                       uint32_t sel) {
-  const bool nxt_in_k = k_fill - kBK < K;  // step k+1 starts one step before k+2
-  half8_t ga[4], gb[4];
-  load_step<K_ALIGNED>(oa, ob, K, k_fill, h, fill);
-  mfma16(acc, fa, fb);
-  dequant_sub<1>(cur, cdpa, cdpb, ga, gb);
-  interleave<4, 16>();
-  mfma16(acc, ga, gb);
-  dequant_sub<2>(cur, cdpa, cdpb, fa, fb);
-  interleave<4, 0>();
-  mfma16(acc, fa, fb);
-  dequant_sub<3>(cur, cdpa, cdpb, ga, gb);
-  interleave<4, 0>();
-  mfma16(acc, ga, gb);
-  scales_of(nxt, nxt_in_k, sel, cdpa, cdpb);
-  dequant_sub<0>(nxt, cdpa, cdpb, fa, fb);
-  interleave<4, 0>();
-}
-
-// Workgroup -> output tile.  Workgroups are dispatched round-robin over the 8
-// XCDs; consecutive ids are first regrouped so that each XCD works on one
-// contiguous range, then ordered in groups of kGroupM tile rows so that the
-// tiles an XCD runs together share A and B rows in its L2.
-__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int* tm, int* tn) {
-  const int nwg = (int)gridDim.x;
-  int b = (int)blockIdx.x;
-  if ((nwg & 7) == 0) b = (b & 7) * (nwg >> 3) + (b >> 3);
-  const int per_group = kGroupM * tiles_n;
-  const int group = b / per_group;
-  const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_group = b - group * per_group;
-  *tm = first_m + in_group % gsize;
-  *tn = in_group / gsize;
-}
-
-template <bool OUT_BF16, bool K_ALIGNED>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmOperand a, GemmOperand b,
-                                                               int64_t K, void* __restrict__ c,
-                                                               int64_t ldc, int tiles_m,
-                                                               int tiles_n) {
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_direct_kernel(GemmOperand a, GemmOperand b,
+                                                                      int64_t K,
+                                                                      void* __restrict__ c,
+                                                                      int64_t ldc, int tiles_m,
+                                                                      int tiles_n) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
@@ -250,69 +306,272 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmOperand a, Ge
   const int h = lane >> 5;
   const OpBase oa = op_base(a, K, m0 + wm * 128 + (lane & 31), h);
   const OpBase ob = op_base(b, K, n0 + wn * 128 + (lane & 31), h);
-
-  float16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // Three raw buffers rotate: step k (being dequantised), k+1 (loaded), k+2
-  // (in flight).  Steps past K load zeros; the loop runs a multiple of 3.
-  StepRaw r0, r1, r2;
-  load_step<K_ALIGNED>(oa, ob, K, 0, h, r0);
-  load_step<K_ALIGNED>(oa, ob, K, kBK, h, r1);
-  half8_t fa[4], fb[4];
-  uint32_t dpa[4], dpb[4];
   // v_perm selector picking scale bytes 2h and 2h+1 (0x0C selects zero)
   const uint32_t sel = h ? 0x0C030C02u : 0x0C010C00u;
-  scales_of(r0, true, sel, dpa, dpb);
-  dequant_sub<0>(r0, dpa, dpb, fa, fb);
+
+  float16_t acc[4][4];
+  zero_acc(acc);
+
+  // Three raw buffers rotate: step k (being dequantised), k+1 (loaded), k+2
+  // (loading during step k).  The loop runs a multiple of 3 steps; steps
+  // past K add zeros.
+  StepRaw r0, r1, r2;
+  {
+    DirectMem first{oa, ob, K, 0, h, r0}, second{oa, ob, K, kBK, h, r1};
+#pragma unroll
+    for (int G = 0; G < 8; ++G) first(G);
+#pragma unroll
+    for (int G = 0; G < 8; ++G) second(G);
+  }
+  Frags f;
+  uint32_t dp[8];
+  first_frags(r0, sel, f, dp);
   for (int64_t kt = 0; kt < nk; kt += 3) {
-    k_step<K_ALIGNED>(acc, fa, fb, dpa, dpb, r0, r1, r2, oa, ob, K, (kt + 2) * kBK, h, sel);
-    k_step<K_ALIGNED>(acc, fa, fb, dpa, dpb, r1, r2, r0, oa, ob, K, (kt + 3) * kBK, h, sel);
-    k_step<K_ALIGNED>(acc, fa, fb, dpa, dpb, r2, r0, r1, oa, ob, K, (kt + 4) * kBK, h, sel);
+    DirectMem l2{oa, ob, K, (kt + 2) * kBK, h, r2};
+    k_step(acc, f, dp, r0, r1, (kt + 1) * kBK < K, sel, l2);
+    DirectMem l0{oa, ob, K, (kt + 3) * kBK, h, r0};
+    k_step(acc, f, dp, r1, r2, (kt + 2) * kBK < K, sel, l0);
+    DirectMem l1{oa, ob, K, (kt + 4) * kBK, h, r1};
+    k_step(acc, f, dp, r2, r0, (kt + 3) * kBK < K, sel, l1);
   }
 
   const float gab = (*a.global) * (*b.global) * 65536.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
-        if (m < a.rows && n < b.rows) {
-          const float v = acc[i][j][r] * gab;
-          if (OUT_BF16)
-            static_cast<uint16_t*>(c)[m * ldc + n] = f32_to_bf16_rne(v);
-          else
-            static_cast<float*>(c)[m * ldc + n] = v;
-        }
-      }
+  store_tile<OUT_BF16>(acc, gab, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, c, ldc);
 }
 
-template <bool OUT_BF16, bool K_ALIGNED>
+// ------------------------------------------------------------ slab kernel
+//
+// LDS map (bytes).  Slab buffer u (0..3) holds K columns [128 s, 128 s + 128)
+// of slab s = u (mod 4):
+//   A codes  [u][256 rows][64 B]  at      0 + 16384 u
+//   B codes  [u][256 rows][64 B]  at  65536 + 16384 u
+//   A scales [u][256 rows][8 B]   at 131072 +  2048 u
+//   B scales [u][256 rows][8 B]   at 139264 +  2048 u
+// A row's 64 code bytes are four 16-byte chunks (chunk c = K-step c/2, lane
+// half c%2); chunk c of row r sits in slot c ^ ((r >> 2) & 3), so the 16
+// rows one 16-byte LDS read serves per cycle cover all 64 banks.
+constexpr int kSlabK = 128;
+constexpr int kLdsACodes = 0, kLdsBCodes = 65536, kLdsAScales = 131072, kLdsBScales = 139264;
+constexpr int kCodeSlab = 256 * 64, kScaleSlab = 256 * 8;
+constexpr int kLdsBytes = 147456;
+// buffer loads in LDS mode per wave and slab: 4 + 4 code loads, 2 + 2 scale loads
+constexpr int kSlabLoads = 12;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over [base, base + bytes): offsets at or past `bytes` read as 0.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// One buffer load in LDS mode: lane i's `SIZE` bytes at voff + soff land at
+// LDS byte lds + SIZE * i.  Written as asm so that the compiler's wait
+// insertion, which cannot tell the slab buffers apart, does not wait for every
+// slab in flight before each LDS read; the kernel waits on vmcnt itself.
+__device__ __forceinline__ void lds_load16(rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :: "v"(voff), "s"(rs), "s"(lds), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, %3 offen lds"
+               :: "v"(voff), "s"(rs), "s"(lds), "s"(soff) : "memory", "m0");
+}
+
+// s_waitcnt with only vmcnt limited (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | 0x0F00);
+}
+
+// What one wave loads of every slab: its share of both operand tiles.  Code
+// load q (0..15) covers tile rows 16q .. 16q+15, lane i row 16q + i/4 and
+// slot i%4 (chunk (i%4) ^ ((i/16)%4) of that row); scale load q (0..7) covers
+// rows 32q .. 32q+31, lane i row 32q + i/2, dword i%2 of the slab.  Wave w
+// issues code loads 4w .. 4w+3 and scale loads 2w, 2w+1 of both operands.
+struct SlabLoader {
+  rsrc_t ca, cb, sa, sb;        // codes and scales of A and B
+  uint32_t vca, vcb, vsa, vsb;  // per-lane offsets within one load
+  uint32_t soa, sob, ssa, ssb;  // wave-uniform offsets of the wave's first load of slab 0
+  uint32_t code_row_step, scale_row_step_a, scale_row_step_b;  // between consecutive loads
+  uint32_t lds0;                // LDS address of the shared array
+  int wave;
+};
+
+__device__ __forceinline__ void slab_issue(const SlabLoader& L, int slab, int u) {
+  const uint32_t kc = (uint32_t)slab * (kSlabK / 2), ks = (uint32_t)slab * (kSlabK / 16);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t q16 = (uint32_t)(4 * L.wave + q);  // 16-row group of the tile
+    lds_load16(L.ca, L.vca, L.soa + q * L.code_row_step + kc,
+               L.lds0 + kLdsACodes + u * kCodeSlab + q16 * 1024);
+    lds_load16(L.cb, L.vcb, L.sob + q * L.code_row_step + kc,
+               L.lds0 + kLdsBCodes + u * kCodeSlab + q16 * 1024);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t q32 = (uint32_t)(2 * L.wave + q);  // 32-row group of the tile
+    lds_load4(L.sa, L.vsa, L.ssa + q * L.scale_row_step_a + ks,
+              L.lds0 + kLdsAScales + u * kScaleSlab + q32 * 256);
+    lds_load4(L.sb, L.vsb, L.ssb + q * L.scale_row_step_b + ks,
+              L.lds0 + kLdsBScales + u * kScaleSlab + q32 * 256);
+  }
+}
+
+// Per-lane LDS read addresses of the wave's fragments.
+struct SlabReader {
+  uint32_t ca[2], cb[2];  // code address of row block 0 for K-step j (add 2048 per block)
+  uint32_t sa, sb;        // scale address of row block 0 (add 256 per block, 4 per K-step)
+};
+
+// The 16 LDS reads of K-step J of the slab in buffer u (chunks 0..15: A
+// codes, B codes, A scales, B scales of row blocks 0..3).
+template <int J>
+struct SlabMem {
+  const uint8_t* lds;
+  const SlabReader& R;
+  int u;
+  StepRaw& r;
+  __device__ __forceinline__ void operator()(int idx) {
+    const int i = idx & 3;
+    if (idx < 4)
+      r.ca[i] = *reinterpret_cast<const uint4*>(lds + R.ca[J] + u * kCodeSlab + i * 2048);
+    else if (idx < 8)
+      r.cb[i] = *reinterpret_cast<const uint4*>(lds + R.cb[J] + u * kCodeSlab + i * 2048);
+    else if (idx < 12)
+      r.sa[i] = *reinterpret_cast<const uint32_t*>(lds + R.sa + u * kScaleSlab + i * 256 + 4 * J);
+    else
+      r.sb[i] = *reinterpret_cast<const uint32_t*>(lds + R.sb + u * kScaleSlab + i * 256 + 4 * J);
+  }
+};
+
+// Slab s (in LDS buffer u = s % 4): K-step 0 from r0 (reading K-step 1 into
+// r1), then -- once slab s+1 has landed for every wave -- the loads of slab
+// s+3 into the buffer slab s-1 used, and K-step 1 from r1 (reading K-step 0
+// of slab s+1 into r0).  Slabs past K load slab 0 again (into buffers nothing
+// reads any more) and the last K-step reads a buffer it does not use, which
+// keeps every wait count and the loop free of branches: a branch here would
+// make the compiler move the accumulators out of AGPRs.
+__device__ __forceinline__ void slab_step(float16_t (&acc)[4][4], Frags& f, uint32_t (&dp)[8],
+                                          StepRaw& r0, StepRaw& r1, const uint8_t* lds,
+                                          const SlabReader& R, const SlabLoader& L, int s, int ns,
+                                          uint32_t sel) {
+  const int u = s & 3;
+  SlabMem<1> m1{lds, R, u, r1};
+  k_step(acc, f, dp, r0, r1, true, sel, m1);
+  wait_vmcnt<kSlabLoads>();      // this wave's loads of slab s+1 landed (s+2 may be in flight)
+  __builtin_amdgcn_s_barrier();  // ... and every wave's; slab s-1's buffer is free
+  slab_issue(L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3);
+  SlabMem<0> m0{lds, R, (u + 1) & 3, r0};
+  k_step(acc, f, dp, r1, r0, true, sel, m0);
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds_kernel(GemmOperand a, GemmOperand b,
+                                                                   int64_t K,
+                                                                   void* __restrict__ c,
+                                                                   int64_t ldc, int tiles_m,
+                                                                   int tiles_n) {
+  __shared__ __align__(16) uint8_t lds[kLdsBytes];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform per wave
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+  const int ns = (int)(K / kSlabK);
+  const uint32_t row_bytes = (uint32_t)(K / 2), srow_bytes = (uint32_t)(K / 16);
+
+  SlabLoader L;
+  const int sha = a.scale_shift, shb = b.scale_shift;
+  const int64_t srows_a = sha ? (a.rows + 15) >> 4 : a.rows;
+  const int64_t srows_b = shb ? (b.rows + 15) >> 4 : b.rows;
+  L.ca = make_rsrc(a.codes, (uint32_t)(a.rows * row_bytes));
+  L.cb = make_rsrc(b.codes, (uint32_t)(b.rows * row_bytes));
+  L.sa = make_rsrc(a.scales, (uint32_t)(srows_a * srow_bytes));
+  L.sb = make_rsrc(b.scales, (uint32_t)(srows_b * srow_bytes));
+  const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+  L.vca = (uint32_t)(lane >> 2) * row_bytes + 16u * chunk;
+  L.vcb = L.vca;
+  L.vsa = (uint32_t)((lane >> 1) >> sha) * srow_bytes + 4u * (lane & 1);
+  L.vsb = (uint32_t)((lane >> 1) >> shb) * srow_bytes + 4u * (lane & 1);
+  L.code_row_step = 16u * row_bytes;
+  L.scale_row_step_a = (32u >> sha) * srow_bytes;
+  L.scale_row_step_b = (32u >> shb) * srow_bytes;
+  L.soa = (uint32_t)(m0 + 64 * wave) * row_bytes;
+  L.sob = (uint32_t)(n0 + 64 * wave) * row_bytes;
+  L.ssa = (uint32_t)((m0 + 64 * wave) >> sha) * srow_bytes;
+  L.ssb = (uint32_t)((n0 + 64 * wave) >> shb) * srow_bytes;
+  L.lds0 = (uint32_t)(uintptr_t)lds;
+  L.wave = wave;
+
+  // Row block i of the wave is tile rows w*128 + 32 i + (lane & 31).
+  const int h = lane >> 5, rl = lane & 31, sw = (rl >> 2) & 3;
+  SlabReader R;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t slot = (uint32_t)((2 * j + h) ^ sw);
+    R.ca[j] = kLdsACodes + (uint32_t)(wm * 128 + rl) * 64 + 16 * slot;
+    R.cb[j] = kLdsBCodes + (uint32_t)(wn * 128 + rl) * 64 + 16 * slot;
+  }
+  R.sa = kLdsAScales + (uint32_t)(wm * 128 + rl) * 8;
+  R.sb = kLdsBScales + (uint32_t)(wn * 128 + rl) * 8;
+  // v_perm selector picking scale bytes 2h and 2h+1 (0x0C selects zero)
+  const uint32_t sel = h ? 0x0C030C02u : 0x0C010C00u;
+
+  float16_t acc[4][4];
+  zero_acc(acc);
+
+  slab_issue(L, 0, 0);
+  slab_issue(L, 1, 1);
+  slab_issue(L, 2, 2);
+  wait_vmcnt<2 * kSlabLoads>();
+  __builtin_amdgcn_s_barrier();
+
+  StepRaw r0, r1;
+  {
+    SlabMem<0> first{lds, R, 0, r0};
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) first(idx);
+  }
+  Frags f;
+  uint32_t dp[8];
+  first_frags(r0, sel, f, dp);
+  for (int s = 0; s < ns; ++s) slab_step(acc, f, dp, r0, r1, lds, R, L, s, ns, sel);
+  wait_vmcnt<0>();  // no LDS-mode load may outlive the workgroup's LDS
+
+  const float gab = (*a.global) * (*b.global) * 65536.0f;
+  store_tile<OUT_BF16>(acc, gab, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, c, ldc);
+}
+
+// ------------------------------------------------------------ launch
+
+// Shapes the slab kernel takes: at least three slabs (the prologue loads
+// three), and operands it can address with 32-bit buffer offsets.
+static bool slab_eligible(const GemmOperand& op, int64_t K) {
+  return K % kSlabK == 0 && K >= 3 * kSlabK && op.rows * (K / 2) < ((int64_t)1 << 31);
+}
+
+template <bool OUT_BF16>
 static hipError_t launch_gemm_t(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c,
                                 int64_t ldc, hipStream_t s) {
   const int tiles_m = (int)((a.rows + kBM - 1) / kBM);
   const int tiles_n = (int)((b.rows + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_kernel<OUT_BF16, K_ALIGNED>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(kGemmThreads), 0, s, a, b, K, c, ldc, tiles_m, tiles_n);
+  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
+  if (slab_eligible(a, K) && slab_eligible(b, K))
+    hipLaunchKernelGGL((gemm_lds_kernel<OUT_BF16>), grid, block, 0, s, a, b, K, c, ldc, tiles_m,
+                       tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_direct_kernel<OUT_BF16>), grid, block, 0, s, a, b, K, c, ldc,
+                       tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c, int c_dtype,
                        int64_t ldc, hipStream_t s) {
-  const bool aligned = (K % kBK) == 0;
-  if (c_dtype == kDtypeBF16)
-    return aligned ? launch_gemm_t<true, true>(a, b, K, c, ldc, s)
-                   : launch_gemm_t<true, false>(a, b, K, c, ldc, s);
-  return aligned ? launch_gemm_t<false, true>(a, b, K, c, ldc, s)
-                 : launch_gemm_t<false, false>(a, b, K, c, ldc, s);
+  if (c_dtype == kDtypeBF16) return launch_gemm_t<true>(a, b, K, c, ldc, s);
+  return launch_gemm_t<false>(a, b, K, c, ldc, s);
 }
 
 }  // namespace nvfp4

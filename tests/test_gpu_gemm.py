@@ -58,8 +58,12 @@ def test_tiny_config(nv, ws):
         assert_gemm_close(c.float().cpu().numpy(), C, S, dt == torch.bfloat16, f"tiny {dt}")
 
 
+# K % 128 == 0 with K >= 384 takes the LDS-slab kernel (ragged edge tiles,
+# slab counts 3, 4, 5 and 8, so the four-buffer ring wraps at every phase);
+# the other K take the direct-load kernel.
 @pytest.mark.parametrize("M,N,K", [(80, 48, 272), (200, 136, 512), (128, 128, 64), (16, 16, 16),
-                                   (256, 384, 1024), (144, 272, 48)])
+                                   (256, 384, 1024), (144, 272, 48), (528, 400, 640),
+                                   (96, 272, 384)])
 @pytest.mark.parametrize("modes", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_shapes_and_scale_modes(nv, ws, M, N, K, modes):
     if (modes[0] == 1 and M % 16) or (modes[1] == 1 and N % 16):
