@@ -56,7 +56,25 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (5 times) and exit: the "
+                        "known-size reference for scaling HBM byte counters")
     return p.parse_args()
+
+
+def copy_reference(mib: int) -> None:
+    """Five launches of torch's device-to-device copy over `mib` MiB: each
+    reads and writes exactly mib MiB, so a profiler's per-dispatch byte
+    counters over these launches give the counters' scale."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": mib, "launches": 5, "bytes_read_per_launch": n * 4,
+                      "bytes_written_per_launch": n * 4}), flush=True)
 
 
 def cpu_baseline(sample_tokens: int):
@@ -91,6 +109,9 @@ def cpu_baseline(sample_tokens: int):
 
 def main():
     args = parse()
+    if args.copy_mib:
+        copy_reference(args.copy_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path.", file=sys.stderr)

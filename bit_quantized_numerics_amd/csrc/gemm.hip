@@ -123,20 +123,22 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, uint32_t dpair, boo
 // (G/4, G%4) on `src`, then dequantises a quarter of the next sub-step's
 // fragments into `dst` (pairs 2(G%2), 2(G%2)+1 of block G/2: sub-step S+1 of
 // `cur`, or, in sub-step 3, sub-step 0 of `nxt` after converting that block's
-// scales -- zero when `nxt_in_k` is false), and in sub-step 0 the memory
-// operation mem(G) (an LDS or global load of a later K-step).  A scheduling
-// fence after each chunk keeps this order.
-template <int S, class Mem>
+// scales -- zero when `nxt_in_k` is false), and the memory operations
+// mem(G) in sub-step 0 and mem2(G) in sub-step 1 (loads of later K-steps,
+// one per chunk so that no burst of them holds up the MFMA stream).  A
+// scheduling fence after each chunk keeps this order.
+template <int S, class Mem, class Mem2>
 __device__ __forceinline__ void sub_step(float16_t (&acc)[4][4], const Frags& src, Frags& dst,
                                          uint32_t (&dp)[8], const StepRaw& cur,
                                          const StepRaw& nxt, bool nxt_in_k, uint32_t sel,
-                                         Mem& mem) {
+                                         Mem& mem, Mem2& mem2) {
 #pragma unroll
   for (int G = 0; G < 16; ++G) {
     const int i = G >> 2, j = G & 3, b = G >> 1, p0 = 2 * (G & 1);
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(src[i]), as_half8(src[4 + j]),
                                                        acc[i][j], 0, 0, 0);
     if (S == 0) mem(G);
+    if (S == 1) mem2(G);
     if (S < 3) {
       const uint32_t w = word_of(cur, b, S + 1);
       dst[b][p0] = dequant_pair(w, dp[b], S + 1 >= 2, p0);
@@ -152,17 +154,23 @@ __device__ __forceinline__ void sub_step(float16_t (&acc)[4][4], const Frags& sr
   }
 }
 
+// No memory operation.
+struct NoMem {
+  __device__ __forceinline__ void operator()(int) {}
+};
+
 // One K-step of 64: on entry `f` holds sub-step 0 of `cur` and dp its scales;
-// on exit they hold sub-step 0 of `nxt`.  mem(0..15) runs during sub-step 0.
-template <class Mem>
+// on exit they hold sub-step 0 of `nxt`.  mem(0..15) runs during sub-step 0,
+// mem2(0..15) during sub-step 1.
+template <class Mem, class Mem2 = NoMem>
 __device__ __forceinline__ void k_step(float16_t (&acc)[4][4], Frags& f, uint32_t (&dp)[8],
                                        const StepRaw& cur, const StepRaw& nxt, bool nxt_in_k,
-                                       uint32_t sel, Mem& mem) {
+                                       uint32_t sel, Mem& mem, Mem2 mem2 = Mem2()) {
   Frags g;
-  sub_step<0>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem);
-  sub_step<1>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem);
-  sub_step<2>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem);
-  sub_step<3>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem);
+  sub_step<0>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
+  sub_step<1>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
+  sub_step<2>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
+  sub_step<3>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
 }
 
 // Sub-step 0 fragments and scales of the first K-step.
@@ -345,11 +353,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_direct_kernel(GemmOperan
 // of slab s = u (mod 4):
 //   A codes  [u][256 rows][64 B]  at      0 + 16384 u
 //   B codes  [u][256 rows][64 B]  at  65536 + 16384 u
-//   A scales [u][256 rows][8 B]   at 131072 +  2048 u
-//   B scales [u][256 rows][8 B]   at 139264 +  2048 u
+//   A scales [u][2 halves][32][2][4 dwords]  at 131072 +  2048 u
+//   B scales [u][2 halves][32][2][4 dwords]  at 139264 +  2048 u
 // A row's 64 code bytes are four 16-byte chunks (chunk c = K-step c/2, lane
 // half c%2); chunk c of row r sits in slot c ^ ((r >> 2) & 3), so the 16
-// rows one 16-byte LDS read serves per cycle cover all 64 banks.
+// rows one 16-byte LDS read serves per cycle cover all 64 banks.  Scales are
+// grouped for the reader: tile half H (rows 128H ..), lane row rl (0..31) and
+// K-step j hold the scale dwords of rows 128H + 32i + rl, i = 0..3, as one
+// 16-byte group in slot j ^ ((rl >> 3) & 1), so one LDS read returns a lane's
+// scales of all four row blocks, again without bank conflicts.
 constexpr int kSlabK = 128;
 constexpr int kLdsACodes = 0, kLdsBCodes = 65536, kLdsAScales = 131072, kLdsBScales = 139264;
 constexpr int kCodeSlab = 256 * 64, kScaleSlab = 256 * 8;
@@ -387,46 +399,65 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // What one wave loads of every slab: its share of both operand tiles.  Code
 // load q (0..15) covers tile rows 16q .. 16q+15, lane i row 16q + i/4 and
-// slot i%4 (chunk (i%4) ^ ((i/16)%4) of that row); scale load q (0..7) covers
-// rows 32q .. 32q+31, lane i row 32q + i/2, dword i%2 of the slab.  Wave w
-// issues code loads 4w .. 4w+3 and scale loads 2w, 2w+1 of both operands.
+// slot i%4 (chunk (i%4) ^ ((i/16)%4) of that row).  Scale load q (0..7)
+// fills 64 dwords of the scale layout: tile half q/4, lane rows rl = 8(q%4) +
+// i/8, slot (i/4)%2 and row block i%4, i.e. tile row 128(q/4) + 8(q%4) +
+// 32(i%4) + i/8 and K-step ((i/4)%2) ^ (q%2).  Wave w issues code loads
+// 4w .. 4w+3 and scale loads 2w, 2w+1 of both operands.
 struct SlabLoader {
   rsrc_t ca, cb, sa, sb;        // codes and scales of A and B
-  uint32_t vca, vcb, vsa, vsb;  // per-lane offsets within one load
-  uint32_t soa, sob, ssa, ssb;  // wave-uniform offsets of the wave's first load of slab 0
-  uint32_t code_row_step, scale_row_step_a, scale_row_step_b;  // between consecutive loads
+  uint32_t vca, vcb;            // per-lane code offsets within one load
+  uint32_t vsa[2], vsb[2];      // per-lane scale offsets for even and odd q
+  uint32_t soa, sob;            // wave-uniform code offsets of the wave's first load (slab 0)
+  uint32_t ssa[2], ssb[2];      // wave-uniform scale offsets of the wave's two loads (slab 0)
+  uint32_t code_row_step;       // between consecutive code loads
   uint32_t lds0;                // LDS address of the shared array
   int wave;
 };
 
-__device__ __forceinline__ void slab_issue(const SlabLoader& L, int slab, int u) {
+// Load n (0..11) of the wave's share of slab `slab` into LDS buffer u: 0..7
+// codes (A and B alternating, 16-row groups 4w .. 4w+3), 8..11 scales.
+__device__ __forceinline__ void slab_load(const SlabLoader& L, int slab, int u, int n) {
   const uint32_t kc = (uint32_t)slab * (kSlabK / 2), ks = (uint32_t)slab * (kSlabK / 16);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  if (n < 8) {
+    const int q = n >> 1;
     const uint32_t q16 = (uint32_t)(4 * L.wave + q);  // 16-row group of the tile
-    lds_load16(L.ca, L.vca, L.soa + q * L.code_row_step + kc,
-               L.lds0 + kLdsACodes + u * kCodeSlab + q16 * 1024);
-    lds_load16(L.cb, L.vcb, L.sob + q * L.code_row_step + kc,
-               L.lds0 + kLdsBCodes + u * kCodeSlab + q16 * 1024);
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t q32 = (uint32_t)(2 * L.wave + q);  // 32-row group of the tile
-    lds_load4(L.sa, L.vsa, L.ssa + q * L.scale_row_step_a + ks,
-              L.lds0 + kLdsAScales + u * kScaleSlab + q32 * 256);
-    lds_load4(L.sb, L.vsb, L.ssb + q * L.scale_row_step_b + ks,
-              L.lds0 + kLdsBScales + u * kScaleSlab + q32 * 256);
+    if ((n & 1) == 0)
+      lds_load16(L.ca, L.vca, L.soa + q * L.code_row_step + kc,
+                 L.lds0 + kLdsACodes + u * kCodeSlab + q16 * 1024);
+    else
+      lds_load16(L.cb, L.vcb, L.sob + q * L.code_row_step + kc,
+                 L.lds0 + kLdsBCodes + u * kCodeSlab + q16 * 1024);
+  } else if (n < 12) {
+    const int q = (n - 8) >> 1;
+    const uint32_t qs = (uint32_t)(2 * L.wave + q);  // scale load of the tile
+    if ((n & 1) == 0)
+      lds_load4(L.sa, L.vsa[q], L.ssa[q] + ks, L.lds0 + kLdsAScales + u * kScaleSlab + qs * 256);
+    else
+      lds_load4(L.sb, L.vsb[q], L.ssb[q] + ks, L.lds0 + kLdsBScales + u * kScaleSlab + qs * 256);
   }
 }
+
+__device__ __forceinline__ void slab_issue(const SlabLoader& L, int slab, int u) {
+#pragma unroll
+  for (int n = 0; n < kSlabLoads; ++n) slab_load(L, slab, u, n);
+}
+
+// The loads of one slab spread over the chunks of a sub-step (chunks 0..11).
+struct SlabDma {
+  const SlabLoader& L;
+  int slab, u;
+  __device__ __forceinline__ void operator()(int G) { slab_load(L, slab, u, G); }
+};
 
 // Per-lane LDS read addresses of the wave's fragments.
 struct SlabReader {
   uint32_t ca[2], cb[2];  // code address of row block 0 for K-step j (add 2048 per block)
-  uint32_t sa, sb;        // scale address of row block 0 (add 256 per block, 4 per K-step)
+  uint32_t sa[2], sb[2];  // scale group (row blocks 0..3) for K-step j
 };
 
-// The 16 LDS reads of K-step J of the slab in buffer u (chunks 0..15: A
-// codes, B codes, A scales, B scales of row blocks 0..3).
+// The 10 LDS reads of K-step J of the slab in buffer u (chunks 0..3 A codes
+// and 4..7 B codes of row blocks 0..3, 8 A scales, 9 B scales).
 template <int J>
 struct SlabMem {
   const uint8_t* lds;
@@ -439,10 +470,13 @@ struct SlabMem {
       r.ca[i] = *reinterpret_cast<const uint4*>(lds + R.ca[J] + u * kCodeSlab + i * 2048);
     else if (idx < 8)
       r.cb[i] = *reinterpret_cast<const uint4*>(lds + R.cb[J] + u * kCodeSlab + i * 2048);
-    else if (idx < 12)
-      r.sa[i] = *reinterpret_cast<const uint32_t*>(lds + R.sa + u * kScaleSlab + i * 256 + 4 * J);
-    else
-      r.sb[i] = *reinterpret_cast<const uint32_t*>(lds + R.sb + u * kScaleSlab + i * 256 + 4 * J);
+    else if (idx == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + R.sa[J] + u * kScaleSlab);
+      r.sa[0] = v.x; r.sa[1] = v.y; r.sa[2] = v.z; r.sa[3] = v.w;
+    } else if (idx == 9) {
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + R.sb[J] + u * kScaleSlab);
+      r.sb[0] = v.x; r.sb[1] = v.y; r.sb[2] = v.z; r.sb[3] = v.w;
+    }
   }
 };
 
@@ -462,9 +496,8 @@ __device__ __forceinline__ void slab_step(float16_t (&acc)[4][4], Frags& f, uint
   k_step(acc, f, dp, r0, r1, true, sel, m1);
   wait_vmcnt<kSlabLoads>();      // this wave's loads of slab s+1 landed (s+2 may be in flight)
   __builtin_amdgcn_s_barrier();  // ... and every wave's; slab s-1's buffer is free
-  slab_issue(L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3);
   SlabMem<0> m0{lds, R, (u + 1) & 3, r0};
-  k_step(acc, f, dp, r1, r0, true, sel, m0);
+  k_step(acc, f, dp, r1, r0, true, sel, m0, SlabDma{L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3});
 }
 
 template <bool OUT_BF16>
@@ -494,15 +527,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds_kernel(GemmOperand a
   const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
   L.vca = (uint32_t)(lane >> 2) * row_bytes + 16u * chunk;
   L.vcb = L.vca;
-  L.vsa = (uint32_t)((lane >> 1) >> sha) * srow_bytes + 4u * (lane & 1);
-  L.vsb = (uint32_t)((lane >> 1) >> shb) * srow_bytes + 4u * (lane & 1);
   L.code_row_step = 16u * row_bytes;
-  L.scale_row_step_a = (32u >> sha) * srow_bytes;
-  L.scale_row_step_b = (32u >> shb) * srow_bytes;
   L.soa = (uint32_t)(m0 + 64 * wave) * row_bytes;
   L.sob = (uint32_t)(n0 + 64 * wave) * row_bytes;
-  L.ssa = (uint32_t)((m0 + 64 * wave) >> sha) * srow_bytes;
-  L.ssb = (uint32_t)((n0 + 64 * wave) >> shb) * srow_bytes;
+  // Scale load q: lane part 32(i%4) + i/8 rows (< 16 after the 16x16 shift
+  // only through 32(i%4), so the shift splits exactly between the two parts).
+  const uint32_t srow_lane = (uint32_t)(32 * (lane & 3) + (lane >> 3));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int qs = 2 * wave + q;
+    const uint32_t j = (uint32_t)(((lane >> 2) & 1) ^ (qs & 1));
+    L.vsa[q] = (srow_lane >> sha) * srow_bytes + 4u * j;
+    L.vsb[q] = (srow_lane >> shb) * srow_bytes + 4u * j;
+    const int64_t tr = 128 * (qs >> 2) + 8 * (qs & 3);
+    L.ssa[q] = (uint32_t)((m0 + tr) >> sha) * srow_bytes;
+    L.ssb[q] = (uint32_t)((n0 + tr) >> shb) * srow_bytes;
+  }
   L.lds0 = (uint32_t)(uintptr_t)lds;
   L.wave = wave;
 
@@ -515,8 +555,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds_kernel(GemmOperand a
     R.ca[j] = kLdsACodes + (uint32_t)(wm * 128 + rl) * 64 + 16 * slot;
     R.cb[j] = kLdsBCodes + (uint32_t)(wn * 128 + rl) * 64 + 16 * slot;
   }
-  R.sa = kLdsAScales + (uint32_t)(wm * 128 + rl) * 8;
-  R.sb = kLdsBScales + (uint32_t)(wn * 128 + rl) * 8;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t slot = (uint32_t)(j ^ ((rl >> 3) & 1));
+    R.sa[j] = kLdsAScales + (uint32_t)wm * 1024 + (uint32_t)rl * 32 + 16 * slot;
+    R.sb[j] = kLdsBScales + (uint32_t)wn * 1024 + (uint32_t)rl * 32 + 16 * slot;
+  }
   // v_perm selector picking scale bytes 2h and 2h+1 (0x0C selects zero)
   const uint32_t sel = h ? 0x0C030C02u : 0x0C010C00u;
 
