@@ -437,9 +437,10 @@ nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* c
   NVFP4_HIP(launch_quant_tile(dtype, kFRow | kFCol | kFRht | kFSrRow | kFSrCol, ad, s));
 
   // Dgrad: dX = Q(dY) Q(W^T)^T [M, K];  Wgrad: dW = Q((R dY)^T) Q((R X)^T)^T [N, K]
-  NVFP4_HIP(launch_gemm(gemm_operand(&ctx->dyq), gemm_operand(&ctx->wqt), N, dx, kDtypeBF16, K, s));
-  NVFP4_HIP(launch_gemm(gemm_operand(&ctx->dyqt), gemm_operand(&ctx->xqt), M, dw,
-                        dw_dtype == NVFP4_BF16 ? kDtypeBF16 : kDtypeF32, K, s));
+  // (one launch: the Wgrad tiles fill the Dgrad tail)
+  NVFP4_HIP(launch_gemm_pair(gemm_operand(&ctx->dyq), gemm_operand(&ctx->wqt), N, dx, kDtypeBF16,
+                             K, gemm_operand(&ctx->dyqt), gemm_operand(&ctx->xqt), M, dw,
+                             dw_dtype == NVFP4_BF16 ? kDtypeBF16 : kDtypeF32, K, s));
   return NVFP4_OK;
 }
 

@@ -187,21 +187,46 @@ __device__ __forceinline__ void first_frags(const StepRaw& r, uint32_t sel, Frag
 
 // ------------------------------------------------------------ tiles, output
 
-// Workgroup -> output tile.  Workgroups are dispatched round-robin over the 8
-// XCDs; consecutive ids are first regrouped so that each XCD works on one
-// contiguous range, then ordered in groups of kGroupM tile rows so that the
-// tiles an XCD runs together share A and B rows in its L2.
-__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int* tm, int* tn) {
-  const int nwg = (int)gridDim.x;
-  int b = (int)blockIdx.x;
-  if ((nwg & 7) == 0) b = (b & 7) * (nwg >> 3) + (b >> 3);
+// Local tile index -> (tile row, tile column), in groups of kGroupM tile
+// rows so that the tiles an XCD runs together share A and B rows in its L2.
+__device__ __forceinline__ void group_tile(int local, int tiles_m, int tiles_n, int* tm, int* tn) {
   const int per_group = kGroupM * tiles_n;
-  const int group = b / per_group;
+  const int group = local / per_group;
   const int first_m = group * kGroupM;
   const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_group = b - group * per_group;
+  const int in_group = local - group * per_group;
   *tm = first_m + in_group % gsize;
   *tn = in_group / gsize;
+}
+
+// Workgroup -> (problem, local tile) for a launch of one or two GEMMs with
+// tiles0 and tiles1 tiles.  Workgroups are dispatched round-robin over the 8
+// XCDs, so workgroup b runs on XCD b % 8 as that XCD's (b / 8)-th; when both
+// tile counts are multiples of 8, XCD x is given tiles [x T/8, (x+1) T/8) of
+// problem 0 first and then the same share of problem 1: each XCD works on
+// contiguous (L2-sharing) ranges, and the longer problem 0 tiles start first.
+__device__ __forceinline__ void tile_of2(int tiles0, int tiles1, int* prob, int* local) {
+  const int b = (int)blockIdx.x;
+  if ((tiles0 & 7) == 0 && (tiles1 & 7) == 0) {
+    const int x = b & 7, pos = b >> 3, per0 = tiles0 >> 3;
+    if (pos < per0) {
+      *prob = 0;
+      *local = x * per0 + pos;
+    } else {
+      *prob = 1;
+      *local = x * (tiles1 >> 3) + (pos - per0);
+    }
+  } else {
+    *prob = b < tiles0 ? 0 : 1;
+    *local = b < tiles0 ? b : b - tiles0;
+  }
+}
+
+// Single-GEMM form for the direct kernel.
+__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int* tm, int* tn) {
+  int prob, local;
+  tile_of2(tiles_m * tiles_n, 0, &prob, &local);
+  group_tile(local, tiles_m, tiles_n, tm, tn);
 }
 
 __device__ __forceinline__ void zero_acc(float16_t (&acc)[4][4]) {
@@ -500,18 +525,30 @@ __device__ __forceinline__ void slab_step(float16_t (&acc)[4][4], Frags& f, uint
   k_step(acc, f, dp, r1, r0, true, sel, m0, SlabDma{L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3});
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds_kernel(GemmOperand a, GemmOperand b,
-                                                                   int64_t K,
-                                                                   void* __restrict__ c,
-                                                                   int64_t ldc, int tiles_m,
-                                                                   int tiles_n) {
+// One GEMM of a slab-kernel launch.
+struct GemmProblem {
+  GemmOperand a, b;
+  int64_t K;
+  void* c;
+  int64_t ldc;
+  int tiles_m, tiles_n;
+};
+
+// One launch computes the tiles of up to two GEMMs (problem 1 has zero tiles
+// when there is only one); OUT0/OUT1_BF16 select each problem's C dtype.
+template <bool OUT0_BF16, bool OUT1_BF16>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds_kernel(GemmProblem p0,
+                                                                   GemmProblem p1) {
   __shared__ __align__(16) uint8_t lds[kLdsBytes];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform per wave
   const int wm = wave >> 1, wn = wave & 1;
-  int tm, tn;
-  tile_of(tiles_m, tiles_n, &tm, &tn);
+  int prob, local, tm, tn;
+  tile_of2(p0.tiles_m * p0.tiles_n, p1.tiles_m * p1.tiles_n, &prob, &local);
+  const GemmProblem& P = prob ? p1 : p0;
+  const GemmOperand a = P.a, b = P.b;
+  const int64_t K = P.K;
+  group_tile(local, P.tiles_m, P.tiles_n, &tm, &tn);
   const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
   const int ns = (int)(K / kSlabK);
   const uint32_t row_bytes = (uint32_t)(K / 2), srow_bytes = (uint32_t)(K / 16);
@@ -586,7 +623,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds_kernel(GemmOperand a
   wait_vmcnt<0>();  // no LDS-mode load may outlive the workgroup's LDS
 
   const float gab = (*a.global) * (*b.global) * 65536.0f;
-  store_tile<OUT_BF16>(acc, gab, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, c, ldc);
+  if (OUT0_BF16 == OUT1_BF16 || prob == 0)
+    store_tile<OUT0_BF16>(acc, gab, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, P.c,
+                          P.ldc);
+  else
+    store_tile<OUT1_BF16>(acc, gab, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, P.c,
+                          P.ldc);
 }
 
 // ------------------------------------------------------------ launch
@@ -597,25 +639,79 @@ static bool slab_eligible(const GemmOperand& op, int64_t K) {
   return K % kSlabK == 0 && K >= 3 * kSlabK && op.rows * (K / 2) < ((int64_t)1 << 31);
 }
 
-template <bool OUT_BF16>
-static hipError_t launch_gemm_t(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c,
-                                int64_t ldc, hipStream_t s) {
-  const int tiles_m = (int)((a.rows + kBM - 1) / kBM);
-  const int tiles_n = (int)((b.rows + kBN - 1) / kBN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
-  if (slab_eligible(a, K) && slab_eligible(b, K))
-    hipLaunchKernelGGL((gemm_lds_kernel<OUT_BF16>), grid, block, 0, s, a, b, K, c, ldc, tiles_m,
-                       tiles_n);
+static GemmProblem make_problem(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c,
+                                int64_t ldc) {
+  GemmProblem p;
+  p.a = a;
+  p.b = b;
+  p.K = K;
+  p.c = c;
+  p.ldc = ldc;
+  p.tiles_m = (int)((a.rows + kBM - 1) / kBM);
+  p.tiles_n = (int)((b.rows + kBN - 1) / kBN);
+  return p;
+}
+
+static bool slab_ok(const GemmProblem& p) {
+  return slab_eligible(p.a, p.K) && slab_eligible(p.b, p.K);
+}
+
+template <bool OUT0, bool OUT1>
+static hipError_t launch_slab(const GemmProblem& p0, const GemmProblem& p1, hipStream_t s) {
+  const int n = p0.tiles_m * p0.tiles_n + p1.tiles_m * p1.tiles_n;
+  hipLaunchKernelGGL((gemm_lds_kernel<OUT0, OUT1>), dim3((unsigned)n), dim3(kGemmThreads), 0, s,
+                     p0, p1);
+  return hipGetLastError();
+}
+
+static hipError_t launch_slab_dt(const GemmProblem& p0, bool bf0, const GemmProblem& p1, bool bf1,
+                                 hipStream_t s) {
+  if (bf0 && bf1) return launch_slab<true, true>(p0, p1, s);
+  if (!bf0 && !bf1) return launch_slab<false, false>(p0, p1, s);
+  if (bf0) return launch_slab<true, false>(p0, p1, s);
+  return launch_slab<true, false>(p1, p0, s);  // bf16 problem first
+}
+
+static GemmProblem no_problem() {
+  GemmProblem p{};
+  p.tiles_m = p.tiles_n = 0;
+  return p;
+}
+
+static hipError_t launch_direct(const GemmProblem& p, bool bf16, hipStream_t s) {
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kGemmThreads);
+  if (bf16)
+    hipLaunchKernelGGL((gemm_direct_kernel<true>), grid, block, 0, s, p.a, p.b, p.K, p.c, p.ldc,
+                       p.tiles_m, p.tiles_n);
   else
-    hipLaunchKernelGGL((gemm_direct_kernel<OUT_BF16>), grid, block, 0, s, a, b, K, c, ldc,
-                       tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_direct_kernel<false>), grid, block, 0, s, p.a, p.b, p.K, p.c, p.ldc,
+                       p.tiles_m, p.tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c, int c_dtype,
                        int64_t ldc, hipStream_t s) {
-  if (c_dtype == kDtypeBF16) return launch_gemm_t<true>(a, b, K, c, ldc, s);
-  return launch_gemm_t<false>(a, b, K, c, ldc, s);
+  const GemmProblem p = make_problem(a, b, K, c, ldc);
+  const bool bf16 = c_dtype == kDtypeBF16;
+  if (slab_ok(p)) return launch_slab_dt(p, bf16, no_problem(), bf16, s);
+  return launch_direct(p, bf16, s);
+}
+
+hipError_t launch_gemm_pair(const GemmOperand& a0, const GemmOperand& b0, int64_t K0, void* c0,
+                            int c0_dtype, int64_t ldc0, const GemmOperand& a1,
+                            const GemmOperand& b1, int64_t K1, void* c1, int c1_dtype,
+                            int64_t ldc1, hipStream_t s) {
+  const GemmProblem p0 = make_problem(a0, b0, K0, c0, ldc0);
+  const GemmProblem p1 = make_problem(a1, b1, K1, c1, ldc1);
+  const bool bf0 = c0_dtype == kDtypeBF16, bf1 = c1_dtype == kDtypeBF16;
+  if (slab_ok(p0) && slab_ok(p1)) {
+    // The problem with more K per tile goes first so its long tiles start first.
+    if (p1.K > p0.K) return launch_slab_dt(p1, bf1, p0, bf0, s);
+    return launch_slab_dt(p0, bf0, p1, bf1, s);
+  }
+  hipError_t e = launch_gemm(a0, b0, K0, c0, c0_dtype, ldc0, s);
+  if (e != hipSuccess) return e;
+  return launch_gemm(a1, b1, K1, c1, c1_dtype, ldc1, s);
 }
 
 }  // namespace nvfp4

@@ -58,5 +58,11 @@ struct GemmOperand {
 
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c,
                        int c_dtype, int64_t ldc, hipStream_t s);
+// Two independent GEMMs in one launch where the kernel allows it (so that the
+// tail of one fills with the tiles of the other), else two launches.
+hipError_t launch_gemm_pair(const GemmOperand& a0, const GemmOperand& b0, int64_t K0, void* c0,
+                            int c0_dtype, int64_t ldc0, const GemmOperand& a1,
+                            const GemmOperand& b1, int64_t K1, void* c1, int c1_dtype,
+                            int64_t ldc1, hipStream_t s);
 
 }  // namespace nvfp4

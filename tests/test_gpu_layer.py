@@ -37,8 +37,12 @@ def _run_layer(nv, M, K, N, seed_base=0):
     return ctx, ops, y, dx, dw, (x, w, dy)
 
 
-def test_layer_small(nv):
-    M, K, N = 256, 384, 512
+# (256, 384, 512): Wgrad has K = 256 and takes the direct-load kernel, Dgrad
+# the slab kernel (two launches).  (640, 272, 640): both backward GEMMs in one
+# slab launch, ragged edge tiles, tile counts not multiples of 8.
+# (512, 2048, 512): one launch with 16 + 16 tiles (the XCD-interleaved order).
+@pytest.mark.parametrize("M,K,N", [(256, 384, 512), (640, 272, 640), (512, 2048, 512)])
+def test_layer_small(nv, M, K, N):
     ctx, ops, y, dx, dw, _ = _run_layer(nv, M, K, N, seed_base=10)
     for out, (a, b), bf16, what in ((y, ("xq", "wq"), True, "Y"), (dx, ("dyq", "wqt"), True, "dX"),
                                     (dw, ("dyqt", "xqt"), False, "dW")):
