@@ -69,16 +69,20 @@ constexpr int kGroupM = 8;  // tile-row group for L2 reuse
 // ------------------------------------------------------------ inner loop
 
 // The codes and scales one lane needs for one K-step: for each of its 4 A and
-// 4 B 32-row blocks, 32 codes (16 bytes: k = 32h .. 32h+31 of the step) and
+// NB B 32-row blocks, 32 codes (16 bytes: k = 32h .. 32h+31 of the step) and
 // the row's four E4M3 scale bytes of the step (the lane uses bytes 2h, 2h+1).
-struct StepRaw {
-  uint4 ca[4], cb[4];
-  uint32_t sa[4], sb[4];
+template <int NB>
+struct StepRawT {
+  uint4 ca[4], cb[NB];
+  uint32_t sa[4], sb[NB];
 };
 
 // Fragments of one MFMA sub-step as packed half2 words: [block][pair], blocks
-// 0..3 the wave's A row blocks, 4..7 its B row blocks.
-typedef uint32_t Frags[8][4];
+// 0..3 the wave's A row blocks, 4..3+NB its B row blocks.
+template <int NB>
+struct FragsT {
+  uint32_t w[4 + NB][4];
+};
 
 __device__ __forceinline__ half8_t as_half8(const uint32_t (&w)[4]) {
   half8_t h;
@@ -87,9 +91,15 @@ __device__ __forceinline__ half8_t as_half8(const uint32_t (&w)[4]) {
 }
 
 // Word S (the codes of sub-step S) of block b of a K-step.
-__device__ __forceinline__ uint32_t word_of(const StepRaw& r, int b, int S) {
+template <int NB>
+__device__ __forceinline__ uint32_t word_of(const StepRawT<NB>& r, int b, int S) {
   const uint4& v = b < 4 ? r.ca[b] : r.cb[b - 4];
   return S == 0 ? v.x : S == 1 ? v.y : S == 2 ? v.z : v.w;
+}
+
+template <int NB>
+__device__ __forceinline__ uint32_t scale_of(const StepRawT<NB>& r, int b) {
+  return b < 4 ? r.sa[b] : r.sb[b - 4];
 }
 
 // Two of the four E4M3 scale bytes in s -> two fp16 values d * 2^-8 (bit
@@ -119,36 +129,38 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, uint32_t dpair, boo
   return o;
 }
 
-// MFMA sub-step S of a K-step, written in issue order: chunk G issues MFMA
-// (G/4, G%4) on `src`, then dequantises a quarter of the next sub-step's
-// fragments into `dst` (pairs 2(G%2), 2(G%2)+1 of block G/2: sub-step S+1 of
-// `cur`, or, in sub-step 3, sub-step 0 of `nxt` after converting that block's
-// scales -- zero when `nxt_in_k` is false), and the memory operations
-// mem(G) in sub-step 0 and mem2(G) in sub-step 1 (loads of later K-steps,
-// one per chunk so that no burst of them holds up the MFMA stream).  A
-// scheduling fence after each chunk keeps this order.
-template <int S, class Mem, class Mem2>
-__device__ __forceinline__ void sub_step(float16_t (&acc)[4][4], const Frags& src, Frags& dst,
-                                         uint32_t (&dp)[8], const StepRaw& cur,
-                                         const StepRaw& nxt, bool nxt_in_k, uint32_t sel,
-                                         Mem& mem, Mem2& mem2) {
+// MFMA sub-step S of a K-step, written in issue order: chunk G (0 .. 4 NB-1)
+// issues MFMA (G / NB, G % NB) on `src`, then dequantises the next
+// sub-step's fragment pairs PP G .. PP G + PP-1 into `dst` (PP = 2 for NB = 4,
+// 3 for NB = 2; pair P is pair P % 4 of block P / 4): sub-step S+1 of `cur`,
+// or, in sub-step 3, sub-step 0 of `nxt` after converting that block's scales
+// (zero when `nxt_in_k` is false); and the memory operations mem(G) in
+// sub-step 0 and mem2(G) in sub-step 1 (loads of later K-steps, one per chunk
+// so that no burst of them holds up the MFMA stream).  A scheduling fence
+// after each chunk keeps this order.
+template <int S, int NB, class Mem, class Mem2>
+__device__ __forceinline__ void sub_step(float16_t (&acc)[4][NB], const FragsT<NB>& src,
+                                         FragsT<NB>& dst, uint32_t (&dp)[4 + NB],
+                                         const StepRawT<NB>& cur, const StepRawT<NB>& nxt,
+                                         bool nxt_in_k, uint32_t sel, Mem& mem, Mem2& mem2) {
+  constexpr int PP = (4 + NB) * 4 / (4 * NB);
+  static_assert(PP * 4 * NB == (4 + NB) * 4, "pairs must split evenly over the MFMAs");
 #pragma unroll
-  for (int G = 0; G < 16; ++G) {
-    const int i = G >> 2, j = G & 3, b = G >> 1, p0 = 2 * (G & 1);
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(src[i]), as_half8(src[4 + j]),
+  for (int G = 0; G < 4 * NB; ++G) {
+    const int i = G / NB, j = G % NB;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(src.w[i]), as_half8(src.w[4 + j]),
                                                        acc[i][j], 0, 0, 0);
     if (S == 0) mem(G);
     if (S == 1) mem2(G);
-    if (S < 3) {
-      const uint32_t w = word_of(cur, b, S + 1);
-      dst[b][p0] = dequant_pair(w, dp[b], S + 1 >= 2, p0);
-      dst[b][p0 + 1] = dequant_pair(w, dp[b], S + 1 >= 2, p0 + 1);
-    } else {
-      if ((G & 1) == 0)
-        dp[b] = nxt_in_k ? scale_pair(b < 4 ? nxt.sa[b] : nxt.sb[b - 4], sel) : 0u;
-      const uint32_t w = word_of(nxt, b, 0);
-      dst[b][p0] = dequant_pair(w, dp[b], false, p0);
-      dst[b][p0 + 1] = dequant_pair(w, dp[b], false, p0 + 1);
+#pragma unroll
+    for (int q = 0; q < PP; ++q) {
+      const int P = PP * G + q, b = P >> 2, p = P & 3;
+      if (S < 3) {
+        dst.w[b][p] = dequant_pair(word_of(cur, b, S + 1), dp[b], S + 1 >= 2, p);
+      } else {
+        if (p == 0) dp[b] = nxt_in_k ? scale_pair(scale_of(nxt, b), sel) : 0u;
+        dst.w[b][p] = dequant_pair(word_of(nxt, b, 0), dp[b], false, p);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -160,13 +172,14 @@ struct NoMem {
 };
 
 // One K-step of 64: on entry `f` holds sub-step 0 of `cur` and dp its scales;
-// on exit they hold sub-step 0 of `nxt`.  mem(0..15) runs during sub-step 0,
-// mem2(0..15) during sub-step 1.
-template <class Mem, class Mem2 = NoMem>
-__device__ __forceinline__ void k_step(float16_t (&acc)[4][4], Frags& f, uint32_t (&dp)[8],
-                                       const StepRaw& cur, const StepRaw& nxt, bool nxt_in_k,
-                                       uint32_t sel, Mem& mem, Mem2 mem2 = Mem2()) {
-  Frags g;
+// on exit they hold sub-step 0 of `nxt`.  mem(G) runs during sub-step 0,
+// mem2(G) during sub-step 1.
+template <int NB, class Mem, class Mem2 = NoMem>
+__device__ __forceinline__ void k_step(float16_t (&acc)[4][NB], FragsT<NB>& f,
+                                       uint32_t (&dp)[4 + NB], const StepRawT<NB>& cur,
+                                       const StepRawT<NB>& nxt, bool nxt_in_k, uint32_t sel,
+                                       Mem& mem, Mem2 mem2 = Mem2()) {
+  FragsT<NB> g;
   sub_step<0>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
   sub_step<1>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
   sub_step<2>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
@@ -174,14 +187,15 @@ __device__ __forceinline__ void k_step(float16_t (&acc)[4][4], Frags& f, uint32_
 }
 
 // Sub-step 0 fragments and scales of the first K-step.
-__device__ __forceinline__ void first_frags(const StepRaw& r, uint32_t sel, Frags& f,
-                                            uint32_t (&dp)[8]) {
+template <int NB>
+__device__ __forceinline__ void first_frags(const StepRawT<NB>& r, uint32_t sel, FragsT<NB>& f,
+                                            uint32_t (&dp)[4 + NB]) {
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    dp[b] = scale_pair(b < 4 ? r.sa[b] : r.sb[b - 4], sel);
+  for (int b = 0; b < 4 + NB; ++b) {
+    dp[b] = scale_pair(scale_of(r, b), sel);
     const uint32_t w = word_of(r, b, 0);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) f[b][p] = dequant_pair(w, dp[b], false, p);
+    for (int p = 0; p < 4; ++p) f.w[b][p] = dequant_pair(w, dp[b], false, p);
   }
 }
 
@@ -229,25 +243,26 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int* tm, int* 
   group_tile(local, tiles_m, tiles_n, tm, tn);
 }
 
-__device__ __forceinline__ void zero_acc(float16_t (&acc)[4][4]) {
+template <int NB>
+__device__ __forceinline__ void zero_acc(float16_t (&acc)[4][NB]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
 // Scaled accumulators -> C (bf16 nearest-even or fp32); rows and columns past
 // the operands are not stored.  (mw, nw) is the wave's first row and column.
-template <bool OUT_BF16>
-__device__ __forceinline__ void store_tile(const float16_t (&acc)[4][4], float gab, int64_t mw,
+template <bool OUT_BF16, int NB>
+__device__ __forceinline__ void store_tile(const float16_t (&acc)[4][NB], float gab, int64_t mw,
                                            int64_t nw, int64_t rows_a, int64_t rows_b, int lane,
                                            void* __restrict__ c, int64_t ldc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = mw + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -315,7 +330,7 @@ struct DirectMem {
   const OpBase& ob;
   int64_t K, k0;
   int h;
-  StepRaw& fill;
+  StepRawT<4>& fill;
   __device__ __forceinline__ void operator()(int G) {
     if (G < 4)
       load_blk(oa, G, K, k0, h, fill.ca[G], fill.sa[G]);
@@ -348,7 +363,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_direct_kernel(GemmOperan
   // Three raw buffers rotate: step k (being dequantised), k+1 (loaded), k+2
   // (loading during step k).  The loop runs a multiple of 3 steps; steps
   // past K add zeros.
-  StepRaw r0, r1, r2;
+  StepRawT<4> r0, r1, r2;
   {
     DirectMem first{oa, ob, K, 0, h, r0}, second{oa, ob, K, kBK, h, r1};
 #pragma unroll
@@ -356,7 +371,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_direct_kernel(GemmOperan
 #pragma unroll
     for (int G = 0; G < 8; ++G) second(G);
   }
-  Frags f;
+  FragsT<4> f;
   uint32_t dp[8];
   first_frags(r0, sel, f, dp);
   for (int64_t kt = 0; kt < nk; kt += 3) {
@@ -391,8 +406,10 @@ constexpr int kSlabK = 128;
 constexpr int kLdsACodes = 0, kLdsBCodes = 65536, kLdsAScales = 131072, kLdsBScales = 139264;
 constexpr int kCodeSlab = 256 * 64, kScaleSlab = 256 * 8;
 constexpr int kLdsBytes = 147456;
-// buffer loads in LDS mode per wave and slab: 4 + 4 code loads, 2 + 2 scale loads
-constexpr int kSlabLoads = 12;
+// A slab is 32 code loads (16 rows x 64 B each, 16 per operand) and 16 scale
+// loads (64 dwords each, 8 per operand) in LDS mode, split evenly over the
+// workgroup's NW waves.
+constexpr int slab_loads(int NW) { return 48 / NW; }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -428,34 +445,39 @@ __device__ __forceinline__ void wait_vmcnt() {
 // fills 64 dwords of the scale layout: tile half q/4, lane rows rl = 8(q%4) +
 // i/8, slot (i/4)%2 and row block i%4, i.e. tile row 128(q/4) + 8(q%4) +
 // 32(i%4) + i/8 and K-step ((i/4)%2) ^ (q%2).  Wave w issues code loads
-// 4w .. 4w+3 and scale loads 2w, 2w+1 of both operands.
+// CG w .. CG w + CG-1 and scale loads SG w .. SG w + SG-1 of both operands
+// (CG = 16/NW, SG = 8/NW).
+template <int NW>
 struct SlabLoader {
-  rsrc_t ca, cb, sa, sb;        // codes and scales of A and B
-  uint32_t vca, vcb;            // per-lane code offsets within one load
-  uint32_t vsa[2], vsb[2];      // per-lane scale offsets for even and odd q
-  uint32_t soa, sob;            // wave-uniform code offsets of the wave's first load (slab 0)
-  uint32_t ssa[2], ssb[2];      // wave-uniform scale offsets of the wave's two loads (slab 0)
-  uint32_t code_row_step;       // between consecutive code loads
-  uint32_t lds0;                // LDS address of the shared array
+  static constexpr int CG = 16 / NW, SG = 8 / NW;
+  rsrc_t ca, cb, sa, sb;          // codes and scales of A and B
+  uint32_t vca, vcb;              // per-lane code offsets within one load
+  uint32_t vsa[SG], vsb[SG];      // per-lane scale offsets of the wave's scale loads
+  uint32_t soa, sob;              // wave-uniform code offsets of the wave's first load (slab 0)
+  uint32_t ssa[SG], ssb[SG];      // wave-uniform scale offsets of the wave's loads (slab 0)
+  uint32_t code_row_step;         // between consecutive code loads
+  uint32_t lds0;                  // LDS address of the shared array
   int wave;
 };
 
-// Load n (0..11) of the wave's share of slab `slab` into LDS buffer u: 0..7
-// codes (A and B alternating, 16-row groups 4w .. 4w+3), 8..11 scales.
-__device__ __forceinline__ void slab_load(const SlabLoader& L, int slab, int u, int n) {
+// Load n (0 .. 48/NW - 1) of the wave's share of slab `slab` into LDS buffer
+// u: first the code loads (A and B alternating), then the scale loads.
+template <int NW>
+__device__ __forceinline__ void slab_load(const SlabLoader<NW>& L, int slab, int u, int n) {
+  constexpr int CG = SlabLoader<NW>::CG, SG = SlabLoader<NW>::SG;
   const uint32_t kc = (uint32_t)slab * (kSlabK / 2), ks = (uint32_t)slab * (kSlabK / 16);
-  if (n < 8) {
+  if (n < 2 * CG) {
     const int q = n >> 1;
-    const uint32_t q16 = (uint32_t)(4 * L.wave + q);  // 16-row group of the tile
+    const uint32_t q16 = (uint32_t)(CG * L.wave + q);  // 16-row group of the tile
     if ((n & 1) == 0)
       lds_load16(L.ca, L.vca, L.soa + q * L.code_row_step + kc,
                  L.lds0 + kLdsACodes + u * kCodeSlab + q16 * 1024);
     else
       lds_load16(L.cb, L.vcb, L.sob + q * L.code_row_step + kc,
                  L.lds0 + kLdsBCodes + u * kCodeSlab + q16 * 1024);
-  } else if (n < 12) {
-    const int q = (n - 8) >> 1;
-    const uint32_t qs = (uint32_t)(2 * L.wave + q);  // scale load of the tile
+  } else if (n < 2 * CG + 2 * SG) {
+    const int q = (n - 2 * CG) >> 1;
+    const uint32_t qs = (uint32_t)(SG * L.wave + q);  // scale load of the tile
     if ((n & 1) == 0)
       lds_load4(L.sa, L.vsa[q], L.ssa[q] + ks, L.lds0 + kLdsAScales + u * kScaleSlab + qs * 256);
     else
@@ -463,14 +485,16 @@ __device__ __forceinline__ void slab_load(const SlabLoader& L, int slab, int u, 
   }
 }
 
-__device__ __forceinline__ void slab_issue(const SlabLoader& L, int slab, int u) {
+template <int NW>
+__device__ __forceinline__ void slab_issue(const SlabLoader<NW>& L, int slab, int u) {
 #pragma unroll
-  for (int n = 0; n < kSlabLoads; ++n) slab_load(L, slab, u, n);
+  for (int n = 0; n < slab_loads(NW); ++n) slab_load(L, slab, u, n);
 }
 
-// The loads of one slab spread over the chunks of a sub-step (chunks 0..11).
+// The loads of one slab spread over the chunks of a sub-step.
+template <int NW>
 struct SlabDma {
-  const SlabLoader& L;
+  const SlabLoader<NW>& L;
   int slab, u;
   __device__ __forceinline__ void operator()(int G) { slab_load(L, slab, u, G); }
 };
@@ -478,29 +502,34 @@ struct SlabDma {
 // Per-lane LDS read addresses of the wave's fragments.
 struct SlabReader {
   uint32_t ca[2], cb[2];  // code address of row block 0 for K-step j (add 2048 per block)
-  uint32_t sa[2], sb[2];  // scale group (row blocks 0..3) for K-step j
+  uint32_t sa[2], sb[2];  // scale group (A: 4 dwords; B: NB dwords) for K-step j
 };
 
-// The 10 LDS reads of K-step J of the slab in buffer u (chunks 0..3 A codes
-// and 4..7 B codes of row blocks 0..3, 8 A scales, 9 B scales).
-template <int J>
+// The LDS reads of K-step J of the slab in buffer u (chunk idx: 0..3 A codes,
+// 4 .. 3+NB B codes of the row blocks, then A scales, then B scales).
+template <int J, int NB>
 struct SlabMem {
   const uint8_t* lds;
   const SlabReader& R;
   int u;
-  StepRaw& r;
+  StepRawT<NB>& r;
   __device__ __forceinline__ void operator()(int idx) {
-    const int i = idx & 3;
-    if (idx < 4)
-      r.ca[i] = *reinterpret_cast<const uint4*>(lds + R.ca[J] + u * kCodeSlab + i * 2048);
-    else if (idx < 8)
-      r.cb[i] = *reinterpret_cast<const uint4*>(lds + R.cb[J] + u * kCodeSlab + i * 2048);
-    else if (idx == 8) {
+    if (idx < 4) {
+      r.ca[idx] = *reinterpret_cast<const uint4*>(lds + R.ca[J] + u * kCodeSlab + idx * 2048);
+    } else if (idx < 4 + NB) {
+      r.cb[idx - 4] =
+          *reinterpret_cast<const uint4*>(lds + R.cb[J] + u * kCodeSlab + (idx - 4) * 2048);
+    } else if (idx == 4 + NB) {
       const uint4 v = *reinterpret_cast<const uint4*>(lds + R.sa[J] + u * kScaleSlab);
       r.sa[0] = v.x; r.sa[1] = v.y; r.sa[2] = v.z; r.sa[3] = v.w;
-    } else if (idx == 9) {
-      const uint4 v = *reinterpret_cast<const uint4*>(lds + R.sb[J] + u * kScaleSlab);
-      r.sb[0] = v.x; r.sb[1] = v.y; r.sb[2] = v.z; r.sb[3] = v.w;
+    } else if (idx == 5 + NB) {
+      if (NB == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + R.sb[J] + u * kScaleSlab);
+        r.sb[0] = v.x; r.sb[1] = v.y; r.sb[NB > 2 ? 2 : 0] = v.z; r.sb[NB > 3 ? 3 : 0] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(lds + R.sb[J] + u * kScaleSlab);
+        r.sb[0] = v.x; r.sb[NB > 1 ? 1 : 0] = v.y;
+      }
     }
   }
 };
@@ -512,17 +541,20 @@ struct SlabMem {
 // reads any more) and the last K-step reads a buffer it does not use, which
 // keeps every wait count and the loop free of branches: a branch here would
 // make the compiler move the accumulators out of AGPRs.
-__device__ __forceinline__ void slab_step(float16_t (&acc)[4][4], Frags& f, uint32_t (&dp)[8],
-                                          StepRaw& r0, StepRaw& r1, const uint8_t* lds,
-                                          const SlabReader& R, const SlabLoader& L, int s, int ns,
-                                          uint32_t sel) {
+template <int NW, int NB>
+__device__ __forceinline__ void slab_step(float16_t (&acc)[4][NB], FragsT<NB>& f,
+                                          uint32_t (&dp)[4 + NB], StepRawT<NB>& r0,
+                                          StepRawT<NB>& r1, const uint8_t* lds,
+                                          const SlabReader& R, const SlabLoader<NW>& L, int s,
+                                          int ns, uint32_t sel) {
   const int u = s & 3;
-  SlabMem<1> m1{lds, R, u, r1};
+  SlabMem<1, NB> m1{lds, R, u, r1};
   k_step(acc, f, dp, r0, r1, true, sel, m1);
-  wait_vmcnt<kSlabLoads>();      // this wave's loads of slab s+1 landed (s+2 may be in flight)
+  wait_vmcnt<slab_loads(NW)>();  // this wave's loads of slab s+1 landed (s+2 may be in flight)
   __builtin_amdgcn_s_barrier();  // ... and every wave's; slab s-1's buffer is free
-  SlabMem<0> m0{lds, R, (u + 1) & 3, r0};
-  k_step(acc, f, dp, r1, r0, true, sel, m0, SlabDma{L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3});
+  SlabMem<0, NB> m0{lds, R, (u + 1) & 3, r0};
+  k_step(acc, f, dp, r1, r0, true, sel, m0,
+         SlabDma<NW>{L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3});
 }
 
 // One GEMM of a slab-kernel launch.
@@ -535,14 +567,17 @@ struct GemmProblem {
 };
 
 // One launch computes the tiles of up to two GEMMs (problem 1 has zero tiles
-// when there is only one); OUT0/OUT1_BF16 select each problem's C dtype.
-template <bool OUT0_BF16, bool OUT1_BF16>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds_kernel(GemmProblem p0,
-                                                                   GemmProblem p1) {
+// when there is only one); OUT0/OUT1_BF16 select each problem's C dtype.  NW
+// waves per workgroup: 2 along M (128 rows each) by NW/2 along N (NB = 8/(NW/2)
+// row blocks of 32 columns each).
+template <bool OUT0_BF16, bool OUT1_BF16, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_lds_kernel(GemmProblem p0, GemmProblem p1) {
+  constexpr int WN = NW / 2, NB = 8 / WN;  // waves along N, B row blocks per wave
+  constexpr int SG = SlabLoader<NW>::SG, CG = SlabLoader<NW>::CG;
   __shared__ __align__(16) uint8_t lds[kLdsBytes];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform per wave
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   int prob, local, tm, tn;
   tile_of2(p0.tiles_m * p0.tiles_n, p1.tiles_m * p1.tiles_n, &prob, &local);
   const GemmProblem& P = prob ? p1 : p0;
@@ -553,7 +588,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds_kernel(GemmProblem p
   const int ns = (int)(K / kSlabK);
   const uint32_t row_bytes = (uint32_t)(K / 2), srow_bytes = (uint32_t)(K / 16);
 
-  SlabLoader L;
+  SlabLoader<NW> L;
   const int sha = a.scale_shift, shb = b.scale_shift;
   const int64_t srows_a = sha ? (a.rows + 15) >> 4 : a.rows;
   const int64_t srows_b = shb ? (b.rows + 15) >> 4 : b.rows;
@@ -565,14 +600,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds_kernel(GemmProblem p
   L.vca = (uint32_t)(lane >> 2) * row_bytes + 16u * chunk;
   L.vcb = L.vca;
   L.code_row_step = 16u * row_bytes;
-  L.soa = (uint32_t)(m0 + 64 * wave) * row_bytes;
-  L.sob = (uint32_t)(n0 + 64 * wave) * row_bytes;
+  L.soa = (uint32_t)(m0 + 16 * CG * wave) * row_bytes;
+  L.sob = (uint32_t)(n0 + 16 * CG * wave) * row_bytes;
   // Scale load q: lane part 32(i%4) + i/8 rows (< 16 after the 16x16 shift
   // only through 32(i%4), so the shift splits exactly between the two parts).
   const uint32_t srow_lane = (uint32_t)(32 * (lane & 3) + (lane >> 3));
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int qs = 2 * wave + q;
+  for (int q = 0; q < SG; ++q) {
+    const int qs = SG * wave + q;
     const uint32_t j = (uint32_t)(((lane >> 2) & 1) ^ (qs & 1));
     L.vsa[q] = (srow_lane >> sha) * srow_bytes + 4u * j;
     L.vsb[q] = (srow_lane >> shb) * srow_bytes + 4u * j;
@@ -583,52 +618,54 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_lds_kernel(GemmProblem p
   L.lds0 = (uint32_t)(uintptr_t)lds;
   L.wave = wave;
 
-  // Row block i of the wave is tile rows w*128 + 32 i + (lane & 31).
+  // A row block i of the wave is tile rows 128 wm + 32 i + (lane & 31); B row
+  // block j is rows 32 NB wn + 32 j + (lane & 31).
   const int h = lane >> 5, rl = lane & 31, sw = (rl >> 2) & 3;
+  const int brow0 = 32 * NB * wn;
   SlabReader R;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const uint32_t slot = (uint32_t)((2 * j + h) ^ sw);
     R.ca[j] = kLdsACodes + (uint32_t)(wm * 128 + rl) * 64 + 16 * slot;
-    R.cb[j] = kLdsBCodes + (uint32_t)(wn * 128 + rl) * 64 + 16 * slot;
+    R.cb[j] = kLdsBCodes + (uint32_t)(brow0 + rl) * 64 + 16 * slot;
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const uint32_t slot = (uint32_t)(j ^ ((rl >> 3) & 1));
     R.sa[j] = kLdsAScales + (uint32_t)wm * 1024 + (uint32_t)rl * 32 + 16 * slot;
-    R.sb[j] = kLdsBScales + (uint32_t)wn * 1024 + (uint32_t)rl * 32 + 16 * slot;
+    // B's NB blocks are dwords (brow0 % 128) / 32 .. of the half's group
+    R.sb[j] = kLdsBScales + (uint32_t)(brow0 >> 7) * 1024 + (uint32_t)rl * 32 + 16 * slot +
+              4u * (uint32_t)((brow0 & 127) >> 5);
   }
   // v_perm selector picking scale bytes 2h and 2h+1 (0x0C selects zero)
   const uint32_t sel = h ? 0x0C030C02u : 0x0C010C00u;
 
-  float16_t acc[4][4];
+  float16_t acc[4][NB];
   zero_acc(acc);
 
   slab_issue(L, 0, 0);
   slab_issue(L, 1, 1);
   slab_issue(L, 2, 2);
-  wait_vmcnt<2 * kSlabLoads>();
+  wait_vmcnt<2 * slab_loads(NW)>();
   __builtin_amdgcn_s_barrier();
 
-  StepRaw r0, r1;
+  StepRawT<NB> r0, r1;
   {
-    SlabMem<0> first{lds, R, 0, r0};
+    SlabMem<0, NB> first{lds, R, 0, r0};
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) first(idx);
+    for (int idx = 0; idx < 6 + NB; ++idx) first(idx);
   }
-  Frags f;
-  uint32_t dp[8];
+  FragsT<NB> f;
+  uint32_t dp[4 + NB];
   first_frags(r0, sel, f, dp);
   for (int s = 0; s < ns; ++s) slab_step(acc, f, dp, r0, r1, lds, R, L, s, ns, sel);
   wait_vmcnt<0>();  // no LDS-mode load may outlive the workgroup's LDS
 
   const float gab = (*a.global) * (*b.global) * 65536.0f;
   if (OUT0_BF16 == OUT1_BF16 || prob == 0)
-    store_tile<OUT0_BF16>(acc, gab, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, P.c,
-                          P.ldc);
+    store_tile<OUT0_BF16>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
   else
-    store_tile<OUT1_BF16>(acc, gab, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, P.c,
-                          P.ldc);
+    store_tile<OUT1_BF16>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
 }
 
 // ------------------------------------------------------------ launch
@@ -656,11 +693,20 @@ static bool slab_ok(const GemmProblem& p) {
   return slab_eligible(p.a, p.K) && slab_eligible(p.b, p.K);
 }
 
+// Waves per slab-kernel workgroup: 4 (one per SIMD, 128 x 128 each) or 8
+// (two per SIMD, 128 x 64 each, 6 instead of 4 dequantisation instructions
+// per MFMA).  Both pass the parity tests and measure within 3% of each other
+// at the layer shapes; 4 is the default.
+#ifndef NVFP4_SLAB_WAVES
+#define NVFP4_SLAB_WAVES 4
+#endif
+constexpr int kSlabWaves = NVFP4_SLAB_WAVES;
+
 template <bool OUT0, bool OUT1>
 static hipError_t launch_slab(const GemmProblem& p0, const GemmProblem& p1, hipStream_t s) {
   const int n = p0.tiles_m * p0.tiles_n + p1.tiles_m * p1.tiles_n;
-  hipLaunchKernelGGL((gemm_lds_kernel<OUT0, OUT1>), dim3((unsigned)n), dim3(kGemmThreads), 0, s,
-                     p0, p1);
+  hipLaunchKernelGGL((gemm_lds_kernel<OUT0, OUT1, kSlabWaves>), dim3((unsigned)n),
+                     dim3(64 * kSlabWaves), 0, s, p0, p1);
   return hipGetLastError();
 }
 
