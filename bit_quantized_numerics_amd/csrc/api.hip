@@ -58,6 +58,8 @@ nvfp4_status check_source(const void* x, int32_t dtype, int64_t rows, int64_t co
   if (rows <= 0 || cols <= 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
   if (rows > (int64_t)65535 * 256) return NVFP4_ERR_SHAPE;  // grid y limit
   if (ld < cols) return NVFP4_ERR_SHAPE;
+  // a 256-row tile of the source must be addressable with 32-bit offsets
+  if (ld * (int64_t)elem_bytes(dtype) * 256 >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   if (!aligned(x, 16) || (ld * (int64_t)elem_bytes(dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
   return NVFP4_OK;
 }
@@ -316,6 +318,7 @@ nvfp4_status nvfp4_rht16(const void* x, float* y, int32_t in_dtype, int64_t rows
   if (axis == 1 && cols % 16 != 0) return NVFP4_ERR_SHAPE;
   if (axis == 0 && (rows % 16 != 0 || cols % 8 != 0)) return NVFP4_ERR_SHAPE;
   if (rows > (int64_t)65535 * 256) return NVFP4_ERR_SHAPE;
+  if (ld * (int64_t)elem_bytes(in_dtype) * 256 >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, 16) || (ld * (int64_t)elem_bytes(in_dtype)) % 16 != 0)
     return NVFP4_ERR_ALIGN;
   NVFP4_HIP(launch_rht16(x, y, in_dtype, rows, cols, ld, axis, rht_signs, as_stream(stream)));

@@ -137,17 +137,20 @@ __device__ __forceinline__ uint32_t fp4x8_rn(const float* v) {
 // Stochastic rounding to E2M1 [Review s10 SR formula; s7 SR example]: with
 // lo <= |v| < hi the neighbouring grid values and T = floor((|v| - lo) /
 // (hi - lo) * 2^22) (the fraction in 22-bit fixed point), round up iff
-// 64 * r16 < T; |v| >= 6 gives 6.  gfx950's stochastic FP4 convert (first
-// element of the pair, unit scale) rounds up iff (rnd >> 10) + T >= 2^22
-// (established by an on-GPU sweep of its rounding), so rnd = ~(r16 << 16),
-// whose top 22 bits are 2^22 - 1 - 64 * r16, reproduces the rule exactly.
-// The code comes back in the low nibble of byte 0 (the compiler does not
-// keep the other bytes of the destination for this instruction, so results
-// are assembled with shifts instead of the byte-select operand).
-__device__ __forceinline__ uint32_t fp4_sr_hw(float v, uint32_t rnd) {
+// 64 * r16 < T; |v| >= 6 gives 6.  gfx950's stochastic FP4 convert of a pair
+// (unit scale) rounds element 0 up iff (rnd >> 10) + T >= 2^22 and element 1
+// up iff ((rnd << 1) >> 10) + T >= 2^22 (both established by on-GPU sweeps of
+// its rounding), so a random operand whose 22-bit field is 2^22 - 1 - 64 r16
+// -- ~(r16 << 16) for element 0, ~(r16 << 15) for element 1 -- reproduces the
+// rule exactly.  The two fields overlap, so each element of a pair gets its
+// own call: the first keeps element 0's code (bits 0..3 of the result), the
+// second element 1's (bits 4..7).
+__device__ __forceinline__ uint32_t fp4x2_sr(float a, float b, uint32_t ra, uint32_t rb) {
   typedef float float2_t __attribute__((ext_vector_type(2)));
-  const float2_t pair = {v, 0.0f};
-  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, rnd, 1.0f, 0) & 0xFu;
+  const float2_t pair = {a, b};
+  const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, ~(ra << 16), 1.0f, 0);
+  const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, pair, ~(rb << 15), 1.0f, 0);
+  return (lo & 0x0Fu) | (hi & 0xF0u);
 }
 
 // ---------------------------------------------------------------- Philox
@@ -163,8 +166,9 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-input xor (truth table 0x96) in one instruction
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -185,13 +189,11 @@ __device__ __forceinline__ U4 sr_draw8(uint64_t seed, uint32_t stream, uint64_t 
 // Eight values -> eight SR codes (value i in nibble i) using the eight 16-bit
 // draws in r (draw i = half i of the 128-bit output, low half first).
 __device__ __forceinline__ uint32_t fp4x8_sr(const float* v, const U4& r) {
-  const uint32_t w[4] = {~r.x, ~r.y, ~r.z, ~r.w};
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
   uint32_t out = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    out |= fp4_sr_hw(v[2 * k], (w[k] << 16) | 0xFFFFu) << (8 * k);
-    out |= fp4_sr_hw(v[2 * k + 1], w[k] | 0xFFFFu) << (8 * k + 4);
-  }
+  for (int k = 0; k < 4; ++k)
+    out |= fp4x2_sr(v[2 * k], v[2 * k + 1], w[k] & 0xFFFFu, w[k] >> 16) << (8 * k);
   return out;
 }
 

@@ -51,17 +51,54 @@ hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t s) {
 
 // ---------------------------------------------------------------- patch load
 
+// One thread's 16 x 8 patch, rows r0 = tile_r0 + prow .. +15, columns
+// c0 .. c0+7, as fp32.  The loads go through a raw buffer over the
+// workgroup's tile rows [tile_r0, tile_r0 + tile_rows), so rows past the
+// matrix read as zeros without a branch and all 16 loads are in flight
+// before the first wait; a column group past `cols` (whole groups only,
+// cols % 8 == 0) reads column 0 and is zeroed afterwards.  Offsets are 32-bit:
+// the entry points require tile_rows * ld * sizeof(TIn) < 2^31.
 template <typename TIn>
-__device__ __forceinline__ void load_patch(const TIn* x, int64_t rows, int64_t ld, int64_t r0,
-                                           int64_t c0, bool valid, float (&v)[16][8]) {
+__device__ __forceinline__ void load_patch(const TIn* x, int64_t tile_r0, int64_t tile_rows,
+                                           int64_t cols, int64_t ld, int prow, int64_t c0,
+                                           float (&v)[16][8]) {
+  constexpr uint32_t kEs = sizeof(TIn);
+  const uint32_t stride = (uint32_t)ld * kEs;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<TIn*>(x + tile_r0 * ld), (short)0, (int)((uint32_t)tile_rows * stride),
+      0x00020000);
+  const bool col_ok = c0 < cols;
+  const uint32_t voff = col_ok ? (uint32_t)prow * stride + (uint32_t)c0 * kEs : 0u;
+  uint32_t raw[16][8 * kEs / 4];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    if (valid && r0 + i < rows) {
-      load8(x + (r0 + i) * ld + c0, v[i]);
+#pragma unroll
+    for (int q = 0; q < (int)(8 * kEs / 16); ++q) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16u * q, (uint32_t)i * stride, 0);
+      raw[i][4 * q + 0] = w[0];
+      raw[i][4 * q + 1] = w[1];
+      raw[i][4 * q + 2] = w[2];
+      raw[i][4 * q + 3] = w[3];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (kEs == 2) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[i][2 * k] = bf16_lo(raw[i][k]);
+        v[i][2 * k + 1] = bf16_hi(raw[i][k]);
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+      for (int k = 0; k < 8; ++k) v[i][k] = __uint_as_float(raw[i][k]);
     }
+  }
+  if (!col_ok) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
   }
 }
 
@@ -79,9 +116,10 @@ __global__ __launch_bounds__(kStatsThreads) void amax_kernel(const TIn* __restri
   const int t = threadIdx.x, cg = t & 31, rs = t >> 5;
   const int64_t r0 = (int64_t)blockIdx.y * kStatsTileR + rs * 16;
   const int64_t c0 = (int64_t)blockIdx.x * kTileC + cg * 8;
-  const bool valid = r0 < rows && c0 < cols;
+  const int64_t tile_r0 = (int64_t)blockIdx.y * kStatsTileR;
   float v[16][8];
-  load_patch(x, rows, ld, r0, c0, valid, v);
+  load_patch(x, tile_r0, min(rows - tile_r0, (int64_t)kStatsTileR), cols, ld, rs * 16, c0, v);
+  (void)r0;
   uint32_t m_raw = 0, m_rht = 0;
   if (RAW) {
 #pragma unroll
@@ -194,7 +232,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
   if (!do_row && !do_col) return;  // uniform across the workgroup
 
   float v[16][8];
-  load_patch(static_cast<const TIn*>(a.x), rows, a.ld, r0, c0, valid, v);
+  load_patch(static_cast<const TIn*>(a.x), tile_r0, min(rows - tile_r0, (int64_t)kTileR), cols,
+             a.ld, rs * 16, c0, v);
 
   if (TWO_D) {
     // ---- one scale per 16x16 tile [Review s2]: this patch and lane ^ 1's
@@ -348,8 +387,9 @@ __global__ __launch_bounds__(kThreads) void rht16_axis0_kernel(const TIn* __rest
   const int64_t c0 = (int64_t)blockIdx.x * kTileC + cg * 8;
   const bool valid = r0 < rows && c0 < cols;
   if (!valid) return;
+  const int64_t tile_r0 = (int64_t)blockIdx.y * kTileR;
   float v[16][8];
-  load_patch(x, rows, ld, r0, c0, valid, v);
+  load_patch(x, tile_r0, min(rows - tile_r0, (int64_t)kTileR), cols, ld, rs * 16, c0, v);
 #pragma unroll
   for (int j = 0; j < 8; ++j) rht16_inplace<8>(&v[0][j], signs);
 #pragma unroll
