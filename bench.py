@@ -39,9 +39,12 @@ BYTES_ROWCOL = 2.0 + 2 * (0.5 + 1.0 / 16)
 BYTES_2D = 2.0 + 2 * (0.5 + 1.0 / 256)
 
 # HBM traffic of the GEMM kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
-# (scaled by a copy kernel's reading), valid only for the kernel source it
-# was measured on.
-GEMM_TRAFFIC = {"source_sha1": None, "bytes_per_launch": None}
+# (KiB per dispatch; FETCH_SIZE x 2 and WRITE_SIZE x 1, the factors a plain
+# 1 GiB device copy reads back), averaged over the single Fprop, Dgrad and
+# Wgrad launches: 1072.7, 875.8 and 1286.5 MB.  Valid only for the kernel
+# source it was measured on (profiles/hbm_traffic_gemm_quantize_*.md).
+GEMM_TRAFFIC = {"source_sha1": "4570dc821782b18f402e5dd83fcab18bd77b88af",
+                "bytes_per_launch": 1078.3e6}
 
 
 def _gemm_source_sha1() -> str:
