@@ -78,6 +78,14 @@ def lib():
         L.oracle_e2m1_sr_index_n.argtypes = [f32p, u32p, i64, u8p]
         L.oracle_sr_bits_n.restype = None
         L.oracle_sr_bits_n.argtypes = [u64, u32, u64, i64, u32p]
+        L.oracle_mx_block.restype = ctypes.c_uint8
+        L.oracle_mx_block.argtypes = [f32p, i32, u8p]
+        L.oracle_mx_quantize.restype = i32
+        L.oracle_mx_quantize.argtypes = [f32p, i64, i64, i64, u8p, u8p]
+        L.oracle_e8m0_decode.restype = ctypes.c_double
+        L.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_mx_dequant.restype = None
+        L.oracle_mx_dequant.argtypes = [u8p, u8p, i64, i64, f64p]
         _lib = L
     return _lib
 
@@ -322,3 +330,55 @@ __all__ = [
     "e2m1_rn_index", "e2m1_sr_index", "e4m3_encode_n", "e2m1_rn_index_n",
     "e2m1_sr_index_n", "linear_operands", "lib",
 ]
+
+
+# ---------------------------------------------------------------- MXFP4
+# The comparator format [Review "Core idea"; method summary s2]: 32-element
+# blocks, one power-of-two (UE8M0) scale each, no tensor scale.  Scale rule
+# (a reading; the pages only describe the format): e = floor(log2(amax_b)) - 2.
+
+
+@dataclasses.dataclass
+class MXTensor:
+    """An MXFP4 operand [rows, cols], blocks of 32 along cols."""
+    codes: np.ndarray   # uint8 [rows, cols/2], even column in the low nibble
+    scales: np.ndarray  # uint8 E8M0 [rows, cols/32]
+    rows: int
+    cols: int
+
+
+def e8m0_decode(code: int) -> float:
+    return lib().oracle_e8m0_decode(code)
+
+
+def mx_block(x) -> tuple:
+    """One block (<= 32 values) -> (E8M0 scale code, 4-bit codes)."""
+    x = _f32(np.asarray(x).reshape(-1))
+    codes = np.zeros(x.size, np.uint8)
+    sc = lib().oracle_mx_block(x, x.size, codes)
+    return int(sc), codes
+
+
+def mx_quantize(x) -> MXTensor:
+    x = _f32(x)
+    R, C = x.shape
+    codes = np.zeros((R, C // 2), np.uint8)
+    scales = np.zeros((R, C // 32), np.uint8)
+    st = lib().oracle_mx_quantize(x, R, C, C, codes, scales)
+    if st != 0:
+        raise OracleError(st)
+    return MXTensor(codes, scales, R, C)
+
+
+def mx_dequant(q: MXTensor) -> np.ndarray:
+    out = np.zeros((q.rows, q.cols), np.float64)
+    lib().oracle_mx_dequant(np.ascontiguousarray(q.codes), np.ascontiguousarray(q.scales),
+                            q.rows, q.cols, out)
+    return out
+
+
+def mx_gemm(a: MXTensor, b: MXTensor):
+    """C = deq(A) deq(B)^T in float64 (library matmul over the dequantised
+    operands) and S = |deq(A)| |deq(B)|^T for the tolerance."""
+    ah, bh = mx_dequant(a), mx_dequant(b)
+    return ah @ bh.T, np.abs(ah) @ np.abs(bh).T

@@ -21,7 +21,8 @@
  * to nearest even (built with -ffp-contract=off, no fast-math); dequantised
  * values and GEMM sums are float64.
  *
- * Parity status: every function here is pinned by a CPU test against values
+ * Parity status: every function here (NVFP4 and the MXFP4 comparator) is
+ * pinned by a CPU test against values
  * the pages print, closed forms, invariants or brute force; see the test
  * files named test_oracle_*.py.
  */
@@ -491,4 +492,99 @@ void oracle_e2m1_sr_index_n(const float* m, const uint32_t* r16, int64_t n, uint
 void oracle_sr_bits_n(uint64_t seed, uint32_t stream, uint64_t e0, int64_t n, uint32_t* out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_sr_bits(seed, stream, e0 + (uint64_t)i);
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4, the comparator format the pages weigh NVFP4 against [Review "Core  */
+/* idea" and s2 of the method summary: blocks of 32 E2M1 values sharing one  */
+/* power-of-two UE8M0 scale, no tensor scale; the pages attribute its loss  */
+/* to that power-of-two rounding dropping a binade (values near +-4, +-6)].  */
+/* The pages do not spell the scale rule out; the reading taken is the OCP  */
+/* Microscaling rule: X = 2^e with e = floor(log2(amax_b)) - 2 (2 is E2M1's */
+/* largest exponent), so amax_b / X lies in [4, 8) and anything at or above */
+/* 6 X saturates to 6 X -- which is exactly the lost binade.  e is clamped  */
+/* to E8M0's range [-127, 127]; an all-zero block stores e = -127 (code 0). */
+/* Elements: v = x / X (exact: a power of two), nearest-even E2M1,          */
+/* saturating.  A block holding Inf or NaN stores the E8M0 NaN code 0xFF    */
+/* and its codes are unspecified (here 0).                                  */
+/* ------------------------------------------------------------------------ */
+
+/* floor(log2(a)) of a positive finite fp32 value, exactly (from its bits). */
+static int floor_log2_f32(float a) {
+  uint32_t b;
+  memcpy(&b, &a, 4);
+  const int ef = (int)((b >> 23) & 0xFF);
+  if (ef > 0) return ef - 127;
+  /* subnormal: value = mantissa * 2^-149 */
+  uint32_t m = b & 0x7FFFFF;
+  int lg = 0;
+  while (m >>= 1) ++lg;
+  return lg - 149;
+}
+
+/* One MX block of n (<= 32) values: returns the E8M0 scale code, writes the
+ * 4-bit codes. */
+uint8_t oracle_mx_block(const float* x, int n, uint8_t* codes) {
+  float amax = 0.0f;
+  int finite = 1;
+  for (int i = 0; i < n; ++i) {
+    if (!isfinite(x[i])) finite = 0;
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  if (!finite) {
+    for (int i = 0; i < n; ++i) codes[i] = 0;
+    return 0xFF;
+  }
+  int e = amax > 0.0f ? floor_log2_f32(amax) - 2 : -127;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  for (int i = 0; i < n; ++i) {
+    const double v = ldexp((double)x[i], -e); /* exact */
+    const double m = fabs(v);
+    /* nearest-even onto the grid on the exact magnitude; m < 8 always, and
+     * anything >= 6 saturates (the page's lost binade) */
+    int idx;
+    if (m >= 6.0)
+      idx = 7;
+    else
+      idx = oracle_e2m1_rn_index((float)m); /* m = |x| 2^-e is exact in fp32 too */
+    codes[i] = (uint8_t)((signbit(x[i]) ? 8 : 0) | idx);
+  }
+  return (uint8_t)(e + 127);
+}
+
+/* MXFP4 quantisation of x [rows, cols] (leading dim ld) with 32-element
+ * blocks along cols (cols % 32 == 0): codes [rows][cols/2] (even column in the
+ * low nibble), scales E8M0 [rows][cols/32]. */
+int oracle_mx_quantize(const float* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
+                       uint8_t* scales) {
+  if (rows <= 0 || cols <= 0 || cols % 32 != 0) return ORACLE_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < rows; ++i) {
+    for (int64_t b = 0; b < cols / 32; ++b) {
+      uint8_t c[32];
+      scales[i * (cols / 32) + b] = oracle_mx_block(x + i * ld + b * 32, 32, c);
+      for (int j = 0; j < 32; j += 2)
+        codes[i * (cols / 2) + b * 16 + j / 2] = (uint8_t)(c[j] | (c[j + 1] << 4));
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* E8M0 scale value 2^(code - 127); code 0xFF is NaN. */
+double oracle_e8m0_decode(uint8_t code) {
+  return code == 0xFF ? NAN : ldexp(1.0, (int)code - 127);
+}
+
+/* Dequantise an MXFP4 operand: x_hat = e2m1(code) * 2^(scale - 127), float64. */
+void oracle_mx_dequant(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t C,
+                       double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < R; ++i)
+    for (int64_t j = 0; j < C; ++j) {
+      uint8_t byte = codes[i * (C / 2) + j / 2];
+      uint8_t code = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+      out[i * C + j] = oracle_e2m1_decode(code) * oracle_e8m0_decode(scales[i * (C / 32) + j / 32]);
+    }
 }
