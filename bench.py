@@ -31,6 +31,7 @@ METRIC = "NVFP4 linear fwd+bwd TFLOP/s + quantize GB/s (8192 tok, 5120→20480)"
 M, K, N = 8192, 5120, 20480
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP4_TFLOPS = 10100.0  # MI355X dense fp4 MFMA (the MXFP4 comparator's dtype)
 
 # Algorithmic bytes of the quantisers, per source element (bf16 input):
 # read 2 B; each copy writes 0.5 B of codes + 1/16 B of 1x16 scales, or
@@ -58,7 +59,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    p.add_argument("--cpu-sample-tokens", type=int, default=8192)
     p.add_argument("--copy-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (5 times) and exit: the "
                         "known-size reference for scaling HBM byte counters")
@@ -108,6 +109,40 @@ def cpu_baseline(sample_tokens: int):
                   f"quantisations + three float64 GEMMs; {t2 - t0:.2f} s",
         "quantize_GBps": qbytes / (t1 - t0) / 1e9,
     }
+
+
+def mxfp4_comparator(nv, x, w, reps: int):
+    """The pages' comparator format on the same Fprop shape: MXFP4 quantisation
+    of X and W (32-element blocks, E8M0 scales) and the GEMM on gfx950's
+    scaled FP4 MFMA (exact products, FP32 accumulation), timed with HIP
+    events on the launch stream."""
+    import torch
+    qx = nv.nvfp4_mx_quantize(x)
+    qw = nv.nvfp4_mx_quantize(w)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    for _ in range(2):
+        nv.nvfp4_mx_quantize(x, qx)
+        nv.nvfp4_mx_quantize(w, qw)
+        nv.nvfp4_gemm(qx, qw, c=y)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tq = tg = 0.0
+    for _ in range(reps):
+        ev[0].record(stream)
+        nv.nvfp4_mx_quantize(x, qx)
+        nv.nvfp4_mx_quantize(w, qw)
+        ev[1].record(stream)
+        nv.nvfp4_gemm(qx, qw, c=y)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        tq += ev[0].elapsed_time(ev[1])
+        tg += ev[1].elapsed_time(ev[2])
+    tq, tg = tq / reps, tg / reps
+    tflops = 2.0 * M * N * K / (tg * 1e-3) / 1e12
+    return {"workload": f"Fprop {M}x{K} by {N}x{K} in MXFP4, bf16 out",
+            "quantize_x_w_ms": round(tq, 4), "gemm_ms": round(tg, 4),
+            "gemm_TFLOPs": round(tflops, 1), "peak_fp4_TFLOPs": PEAK_FP4_TFLOPS,
+            "frac": round(tflops / PEAK_FP4_TFLOPS, 4)}
 
 
 def main():
@@ -210,6 +245,7 @@ def main():
                      "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic},
     }
+    out["mxfp4_comparator"] = mxfp4_comparator(nv, x, w, max(3, args.steps // 2))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

@@ -30,7 +30,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_HIP, ERR_NONFINITE = range(8)
 F32, BF16 = 0, 1
 RN, SR = 0, 1
-SCALE_1X16, SCALE_16X16 = 0, 1
+SCALE_1X16, SCALE_16X16, SCALE_MX32 = 0, 1, 2
 
 
 class c_tensor(ctypes.Structure):
@@ -71,6 +71,7 @@ _SIGS = {
                                      ctypes.POINTER(c_quant_opts), _T, _T, _vp, _sz, _vp]),
     "nvfp4_quantize_2d": (_i32, [_vp, _i32, _i64, _i64, _i64, _T, _T, _vp, _sz, _vp]),
     "nvfp4_rht16": (_i32, [_vp, _vp, _i32, _i64, _i64, _i64, _i32, _u32, _vp]),
+    "nvfp4_mx_quantize": (_i32, [_vp, _i32, _i64, _i64, _i64, _T, _vp]),
     "nvfp4_gemm": (_i32, [_T, _T, _vp, _i32, _i64, _vp, _sz, _vp]),
     "nvfp4_linear_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.POINTER(c_recipe),
                                 ctypes.POINTER(c_linear_ctx), _vp, _sz, _vp]),
@@ -151,6 +152,8 @@ class NVFP4Tensor:
         return self.codes.view(self.rows, self.cols // 2)
 
     def scales_2d(self):
+        if self.scale_mode == SCALE_MX32:
+            return self.scales.view(self.rows, self.cols // 32)
         if self.scale_mode == SCALE_1X16:
             return self.scales.view(self.rows, self.cols // 16)
         return self.scales.view(self.rows // 16, self.cols // 16)
@@ -248,6 +251,18 @@ def nvfp4_rht16(x: torch.Tensor, axis: int, rht_signs: int, y: torch.Tensor | No
                             _dtype_code(x), rows, cols, _ld(x), axis, rht_signs, _stream(x.device)),
            "nvfp4_rht16")
     return y
+
+
+def nvfp4_mx_quantize(x: torch.Tensor, out: NVFP4Tensor | None = None) -> NVFP4Tensor:
+    """MXFP4 comparator quantisation (32-element blocks, E8M0 scales)."""
+    rows, cols = x.shape
+    if out is None:
+        out = NVFP4Tensor(rows, cols, SCALE_MX32, device=x.device)
+    ct = out.c()
+    _check(_lib.nvfp4_mx_quantize(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), rows, cols, _ld(x),
+                                  ctypes.byref(ct), _stream(x.device)), "nvfp4_mx_quantize")
+    out.update(ct)
+    return out
 
 
 def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, c: torch.Tensor | None = None,

@@ -121,9 +121,13 @@ void philox_host(uint32_t c[4], uint32_t k0, uint32_t k1) {
 }
 
 nvfp4_status check_gemm_operand(const nvfp4_tensor* t) {
-  if (!t || !t->codes || !t->scales || !t->global_scale) return NVFP4_ERR_NULL;
+  if (!t || !t->codes || !t->scales) return NVFP4_ERR_NULL;
+  if (t->scale_mode != NVFP4_SCALE_MX32 && !t->global_scale) return NVFP4_ERR_NULL;
   if (t->rows <= 0 || t->cols <= 0 || t->cols % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (t->scale_mode != NVFP4_SCALE_1X16 && t->scale_mode != NVFP4_SCALE_16X16) return NVFP4_ERR_DTYPE;
+  if (t->scale_mode != NVFP4_SCALE_1X16 && t->scale_mode != NVFP4_SCALE_16X16 &&
+      t->scale_mode != NVFP4_SCALE_MX32)
+    return NVFP4_ERR_DTYPE;
+  if (t->scale_mode == NVFP4_SCALE_MX32 && t->cols % 32 != 0) return NVFP4_ERR_SHAPE;
   if (t->scale_mode == NVFP4_SCALE_16X16 && t->rows % 16 != 0) return NVFP4_ERR_SHAPE;
   if (!aligned(t->codes, 16) || !aligned(t->scales, 4) || !aligned(t->global_scale, 4))
     return NVFP4_ERR_ALIGN;
@@ -154,7 +158,10 @@ nvfp4_status nvfp4_tensor_bytes(int64_t rows, int64_t cols, int32_t scale_mode, 
                                 size_t* scales_bytes) {
   if (!codes_bytes || !scales_bytes) return NVFP4_ERR_NULL;
   if (rows <= 0 || cols <= 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (scale_mode == NVFP4_SCALE_1X16) {
+  if (scale_mode == NVFP4_SCALE_MX32) {
+    if (cols % 32 != 0) return NVFP4_ERR_SHAPE;
+    *scales_bytes = (size_t)(rows * (cols / 32));
+  } else if (scale_mode == NVFP4_SCALE_1X16) {
     *scales_bytes = (size_t)(rows * (cols / 16));
   } else if (scale_mode == NVFP4_SCALE_16X16) {
     if (rows % 16 != 0) return NVFP4_ERR_SHAPE;
@@ -337,7 +344,30 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, i
   if (ldc < b->rows) return NVFP4_ERR_SHAPE;
   if ((a->rows + 255) / 256 * ((b->rows + 255) / 256) > (int64_t)0x7FFFFFFF) return NVFP4_ERR_SHAPE;
   if (!aligned(c, 4)) return NVFP4_ERR_ALIGN;
+  const bool mxa = a->scale_mode == NVFP4_SCALE_MX32, mxb = b->scale_mode == NVFP4_SCALE_MX32;
+  if (mxa != mxb) return NVFP4_ERR_DTYPE;
+  if (mxa) {
+    const int64_t K = a->cols;
+    if (K % 128 != 0 || K < 384 || a->rows * (K / 2) >= ((int64_t)1 << 31) ||
+        b->rows * (K / 2) >= ((int64_t)1 << 31))
+      return NVFP4_ERR_SHAPE;
+    NVFP4_HIP(launch_mx_gemm(gemm_operand(a), gemm_operand(b), K, c, c_dtype, ldc,
+                             as_stream(stream)));
+    return NVFP4_OK;
+  }
   NVFP4_HIP(launch_gemm(gemm_operand(a), gemm_operand(b), a->cols, c, c_dtype, ldc, as_stream(stream)));
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                               int64_t ld, nvfp4_tensor* out, void* stream) {
+  NVFP4_TRY(check_source(x, dtype, rows, cols, ld));
+  if (cols % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (!out || !out->codes || !out->scales) return NVFP4_ERR_NULL;
+  if (!aligned(out->codes, 16)) return NVFP4_ERR_ALIGN;
+  set_shape(out, rows, cols, NVFP4_SCALE_MX32);
+  NVFP4_HIP(launch_mx_quantize(x, dtype, rows, cols, ld, out->codes, out->scales,
+                               as_stream(stream)));
   return NVFP4_OK;
 }
 

@@ -45,6 +45,8 @@ hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t s);
 hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                        uint32_t signs, uint32_t* out_raw, uint32_t* out_rht, hipStream_t s);
 hipError_t launch_quant_tile(int dtype, int flags, const TileArgs& a, hipStream_t s);
+hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_rht16(const void* x, float* y, int dtype, int64_t rows, int64_t cols, int64_t ld,
                         int axis, uint32_t signs, hipStream_t s);
 
@@ -58,6 +60,10 @@ struct GemmOperand {
 
 hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c,
                        int c_dtype, int64_t ldc, hipStream_t s);
+// MXFP4 GEMM (32-element blocks, E8M0 scales [rows][K/32]; global unused).
+// Requires K % 128 == 0, K >= 384 and rows * K / 2 < 2^31 for both operands.
+hipError_t launch_mx_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c,
+                          int c_dtype, int64_t ldc, hipStream_t s);
 // Two independent GEMMs in one launch where the kernel allows it (so that the
 // tail of one fills with the tiles of the other), else two launches.
 hipError_t launch_gemm_pair(const GemmOperand& a0, const GemmOperand& b0, int64_t K0, void* c0,

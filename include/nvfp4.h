@@ -65,7 +65,15 @@ typedef enum {
 
 typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
 typedef enum { NVFP4_RN = 0, NVFP4_SR = 1 } nvfp4_round;
-typedef enum { NVFP4_SCALE_1X16 = 0, NVFP4_SCALE_16X16 = 1 } nvfp4_scale_mode;
+/* NVFP4_SCALE_MX32 marks an MXFP4 operand, the comparator format the pages
+ * weigh NVFP4 against [Review "Core idea"; method summary s2]: the same
+ * codes, one E8M0 (power-of-two, bias 127) scale per 32 elements of a row,
+ * scales [rows][cols/32], no tensor scale (global_scale unused, may be NULL). */
+typedef enum {
+  NVFP4_SCALE_1X16 = 0,
+  NVFP4_SCALE_16X16 = 1,
+  NVFP4_SCALE_MX32 = 2
+} nvfp4_scale_mode;
 
 /* One quantised operand (see the format above).  rows x cols is the
  * operand's own logical shape; cols is the block (contraction) axis. */
@@ -193,6 +201,22 @@ nvfp4_status nvfp4_quantize_2d(const void* w, int32_t dtype, int64_t rows, int64
                                void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * nvfp4_mx_quantize: MXFP4 quantisation of x [rows, cols] (leading dim ld,
+ * F32 or BF16) with 32-element blocks along cols (cols % 32 == 0), the
+ * comparator of [Review "Core idea"; method summary s2: blocks of 32, one
+ * power-of-two UE8M0 scale].  Scale rule (the OCP Microscaling one; the
+ * pages describe only the format): e = floor(log2(amax_b)) - 2 clamped to
+ * [-127, 127], stored as e + 127; so amax_b / 2^e is in [4, 8) and values at
+ * or above 6 * 2^e saturate (the binade the pages say MXFP4 loses).  An
+ * all-zero block stores 0; a block holding Inf/NaN stores 0xFF (E8M0 NaN)
+ * and zero codes.  Elements: x * 2^-e (exact), nearest-even E2M1.  out
+ * (codes >= rows*cols/2 bytes, scales >= rows*cols/32) becomes an
+ * NVFP4_SCALE_MX32 operand [rows, cols]; ragged rows are allowed.
+ */
+nvfp4_status nvfp4_mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                               int64_t ld, nvfp4_tensor* out, void* stream);
+
+/*
  * nvfp4_rht16: standalone 16-point random Hadamard transform
  * y = 1/4 * H16 * diag(s) * x on every 16-element chunk [Review s3].
  * axis 1: chunks along each row (cols % 16 == 0); axis 0: along each column
@@ -210,6 +234,11 @@ nvfp4_status nvfp4_rht16(const void* x, float* y, int32_t in_dtype, int64_t rows
  * are contiguous along k (a->cols == b->cols == K); either may use 1x16 or
  * 16x16 scales.  c: [M, N] row-major with leading dim ldc, dtype NVFP4_F32 or
  * NVFP4_BF16.  M, N multiples of 16; K a multiple of 16.
+ * With both operands in NVFP4_SCALE_MX32 mode it is the MXFP4 product
+ * C = sum_k (e2m1 * 2^(s-127))_A (e2m1 * 2^(s-127))_B (no tensor scales), on
+ * gfx950's scaled FP4 MFMA; that path needs K % 128 == 0, K >= 384 and
+ * rows * K / 2 < 2^31 for each operand (else NVFP4_ERR_SHAPE), and mixing an
+ * MX32 operand with an NVFP4 one is NVFP4_ERR_DTYPE.
  */
 nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int32_t c_dtype,
                         int64_t ldc, void* workspace, size_t ws_bytes, void* stream);

@@ -100,6 +100,28 @@ def test_gemm_argument_errors():
     assert f(ctypes.byref(a_mis), ctypes.byref(b), P, nv.F32, 128, None, 0, None) == nv.ERR_ALIGN
 
 
+def test_mx_argument_errors():
+    """MXFP4 comparator paths: argument errors are caught before any launch."""
+    f = nv._lib.nvfp4_gemm
+    mx = nv.c_tensor(P, P, None, 64, 512, nv.SCALE_MX32)     # no tensor scale needed
+    mx_b = nv.c_tensor(P, P, None, 128, 512, nv.SCALE_MX32)
+    nvf = nv.c_tensor(P, P, P, 128, 512, nv.SCALE_1X16)
+    assert f(ctypes.byref(mx), ctypes.byref(nvf), P, nv.F32, 128, None, 0, None) == nv.ERR_DTYPE
+    small_k = nv.c_tensor(P, P, None, 64, 256, nv.SCALE_MX32)
+    small_kb = nv.c_tensor(P, P, None, 128, 256, nv.SCALE_MX32)
+    assert f(ctypes.byref(small_k), ctypes.byref(small_kb), P, nv.F32, 128, None, 0,
+             None) == nv.ERR_SHAPE
+    odd_k = nv.c_tensor(P, P, None, 64, 400, nv.SCALE_MX32)  # cols % 32 != 0
+    assert f(ctypes.byref(odd_k), ctypes.byref(mx_b), P, nv.F32, 128, None, 0, None) == nv.ERR_SHAPE
+    q = nv._lib.nvfp4_mx_quantize
+    out = nv.c_tensor(P, P, None, 0, 0, 0)
+    assert q(P, nv.BF16, 64, 48, 48, ctypes.byref(out), None) == nv.ERR_SHAPE  # cols % 32
+    assert q(None, nv.BF16, 64, 64, 64, ctypes.byref(out), None) == nv.ERR_NULL
+    assert q(P, nv.BF16, 64, 64, 64, None, None) == nv.ERR_NULL
+    cb, sb = nv.nvfp4_tensor_bytes(64, 96, nv.SCALE_MX32)
+    assert (cb, sb) == (64 * 48, 64 * 3)
+
+
 def test_2d_rht_and_layer_argument_errors():
     t = _tensor()
     assert nv._lib.nvfp4_quantize_2d(P, nv.BF16, 40, 32, 32, ctypes.byref(t), None, P, WSB,
