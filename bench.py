@@ -111,6 +111,25 @@ def cpu_baseline(sample_tokens: int):
     }
 
 
+def weight_consistency(nv, w, ws):
+    """w_fprop vs w_bprop [Review s2; Captions Fig. 14]: relative Frobenius
+    difference between the decoded Fprop copy of W and the decoded Dgrad copy
+    (transposed back), with 16x16 scales (the recipe) and with 1x16 scales
+    along each copy's own rows (the ablation)."""
+    import torch
+
+    def rel(a, b):
+        da, db = nv.nvfp4_dequantize(a), nv.nvfp4_dequantize(b).t()
+        return float((torch.linalg.norm(da - db) / torch.linalg.norm(da)).item())
+
+    q2, q2t = nv.nvfp4_quantize_2d(w, ws)
+    r2 = rel(q2, q2t)
+    q1, q1t = nv.nvfp4_quantize(w, ws), nv.nvfp4_quantize(w, ws, transpose=True)
+    r1 = rel(q1, q1t)
+    return {"workload": f"W [{N}, {K}], decoded Fprop copy vs transposed decoded Dgrad copy",
+            "rel_diff_16x16": r2, "rel_diff_1x16": r1}
+
+
 def mxfp4_comparator(nv, x, w, reps: int):
     """The pages' comparator format on the same Fprop shape: MXFP4 quantisation
     of X and W (32-element blocks, E8M0 scales) and the GEMM on gfx950's
@@ -246,6 +265,7 @@ def main():
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic},
     }
     out["mxfp4_comparator"] = mxfp4_comparator(nv, x, w, max(3, args.steps // 2))
+    out["weight_consistency"] = weight_consistency(nv, w, ws)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

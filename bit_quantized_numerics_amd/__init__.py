@@ -46,7 +46,9 @@ class c_quant_opts(ctypes.Structure):
 
 
 class c_recipe(ctypes.Structure):
-    _fields_ = [("rht_signs", ctypes.c_uint32), ("training", ctypes.c_int32)]
+    _fields_ = [("rht_signs", ctypes.c_uint32), ("training", ctypes.c_int32),
+                ("no_2d_weights", ctypes.c_int32), ("no_rht", ctypes.c_int32),
+                ("no_sr", ctypes.c_int32)]
 
 
 class c_linear_ctx(ctypes.Structure):
@@ -72,6 +74,7 @@ _SIGS = {
     "nvfp4_quantize_2d": (_i32, [_vp, _i32, _i64, _i64, _i64, _T, _T, _vp, _sz, _vp]),
     "nvfp4_rht16": (_i32, [_vp, _vp, _i32, _i64, _i64, _i64, _i32, _u32, _vp]),
     "nvfp4_mx_quantize": (_i32, [_vp, _i32, _i64, _i64, _i64, _T, _vp]),
+    "nvfp4_dequantize": (_i32, [_T, _vp, _i64, _vp]),
     "nvfp4_gemm": (_i32, [_T, _T, _vp, _i32, _i64, _vp, _sz, _vp]),
     "nvfp4_linear_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.POINTER(c_recipe),
                                 ctypes.POINTER(c_linear_ctx), _vp, _sz, _vp]),
@@ -149,14 +152,17 @@ class NVFP4Tensor:
         self.rows, self.cols, self.scale_mode = ct.rows, ct.cols, ct.scale_mode
 
     def codes_2d(self):
-        return self.codes.view(self.rows, self.cols // 2)
+        return self.codes[:self.rows * (self.cols // 2)].view(self.rows, self.cols // 2)
 
     def scales_2d(self):
+        """The scale grid of the current scale mode (buffers may be larger)."""
         if self.scale_mode == SCALE_MX32:
-            return self.scales.view(self.rows, self.cols // 32)
-        if self.scale_mode == SCALE_1X16:
-            return self.scales.view(self.rows, self.cols // 16)
-        return self.scales.view(self.rows // 16, self.cols // 16)
+            r, c = self.rows, self.cols // 32
+        elif self.scale_mode == SCALE_1X16:
+            r, c = self.rows, self.cols // 16
+        else:
+            r, c = self.rows // 16, self.cols // 16
+        return self.scales[:r * c].view(r, c)
 
 
 # ------------------------------------------------------------------ calls
@@ -253,6 +259,16 @@ def nvfp4_rht16(x: torch.Tensor, axis: int, rht_signs: int, y: torch.Tensor | No
     return y
 
 
+def nvfp4_dequantize(t: NVFP4Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode an operand to fp32 [rows, cols]."""
+    if out is None:
+        out = torch.empty(t.rows, t.cols, dtype=torch.float32, device=t.codes.device)
+    ct = t.c()
+    _check(_lib.nvfp4_dequantize(ctypes.byref(ct), ctypes.c_void_p(out.data_ptr()), _ld(out),
+                                 _stream(out.device)), "nvfp4_dequantize")
+    return out
+
+
 def nvfp4_mx_quantize(x: torch.Tensor, out: NVFP4Tensor | None = None) -> NVFP4Tensor:
     """MXFP4 comparator quantisation (32-element blocks, E8M0 scales)."""
     rows, cols = x.shape
@@ -282,8 +298,9 @@ class LinearContext:
     def __init__(self, M: int, K: int, N: int, device="cuda"):
         self.M, self.K, self.N = M, K, N
         self.xq = NVFP4Tensor(M, K, device=device)
-        self.wq = NVFP4Tensor(N, K, SCALE_16X16, device=device)
-        self.wqt = NVFP4Tensor(K, N, SCALE_16X16, device=device)
+        # 1x16-sized scale buffers: large enough for either weight recipe
+        self.wq = NVFP4Tensor(N, K, SCALE_1X16, device=device)
+        self.wqt = NVFP4Tensor(K, N, SCALE_1X16, device=device)
         self.xqt = NVFP4Tensor(K, M, device=device)
         self.dyq = NVFP4Tensor(M, N, device=device)
         self.dyqt = NVFP4Tensor(N, M, device=device)
@@ -295,13 +312,18 @@ class LinearContext:
             getattr(self, name).update(getattr(self.cctx, name))
 
 
+def _recipe(rht_signs, training, no_2d_weights, no_rht, no_sr):
+    return c_recipe(int(rht_signs), int(training), int(no_2d_weights), int(no_rht), int(no_sr))
+
+
 def nvfp4_linear_fwd(x: torch.Tensor, w: torch.Tensor, ctx: LinearContext, ws: Workspace,
-                     rht_signs: int, training: bool = True, y: torch.Tensor | None = None):
+                     rht_signs: int, training: bool = True, y: torch.Tensor | None = None, *,
+                     no_2d_weights: bool = False, no_rht: bool = False, no_sr: bool = False):
     M, K = x.shape
     N = w.shape[0]
     if y is None:
         y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
-    rec = c_recipe(rht_signs, int(training))
+    rec = _recipe(rht_signs, training, no_2d_weights, no_rht, no_sr)
     _check(_lib.nvfp4_linear_fwd(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
                                  ctypes.c_void_p(y.data_ptr()), M, K, N, _dtype_code(x),
                                  ctypes.byref(rec), ctypes.byref(ctx.cctx), ws.ptr, ws.nbytes,
@@ -312,12 +334,13 @@ def nvfp4_linear_fwd(x: torch.Tensor, w: torch.Tensor, ctx: LinearContext, ws: W
 
 def nvfp4_linear_bwd(dy: torch.Tensor, ctx: LinearContext, ws: Workspace, rht_signs: int,
                      sr_seed: int, dw_dtype=torch.float32, dx: torch.Tensor | None = None,
-                     dw: torch.Tensor | None = None):
+                     dw: torch.Tensor | None = None, *, no_2d_weights: bool = False,
+                     no_rht: bool = False, no_sr: bool = False):
     if dx is None:
         dx = torch.empty(ctx.M, ctx.K, dtype=torch.bfloat16, device=dy.device)
     if dw is None:
         dw = torch.empty(ctx.N, ctx.K, dtype=dw_dtype, device=dy.device)
-    rec = c_recipe(rht_signs, 1)
+    rec = _recipe(rht_signs, True, no_2d_weights, no_rht, no_sr)
     _check(_lib.nvfp4_linear_bwd(ctypes.c_void_p(dy.data_ptr()), _dtype_code(dy), ctypes.byref(ctx.cctx),
                                  ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(dw.data_ptr()),
                                  _dtype_code(dw), sr_seed, ctypes.byref(rec), ws.ptr, ws.nbytes,

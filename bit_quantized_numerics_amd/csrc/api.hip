@@ -359,6 +359,16 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, i
   return NVFP4_OK;
 }
 
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor* t, float* out, int64_t ldo, void* stream) {
+  NVFP4_TRY(check_gemm_operand(t));
+  if (!out) return NVFP4_ERR_NULL;
+  if (ldo < t->cols || ldo % 4 != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned(out, 16) || !aligned(t->codes, 4)) return NVFP4_ERR_ALIGN;
+  NVFP4_HIP(launch_dequant(t->codes, t->scales, t->global_scale, t->rows, t->cols, t->scale_mode,
+                           out, ldo, as_stream(stream)));
+  return NVFP4_OK;
+}
+
 nvfp4_status nvfp4_mx_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols,
                                int64_t ld, nvfp4_tensor* out, void* stream) {
   NVFP4_TRY(check_source(x, dtype, rows, cols, ld));
@@ -389,9 +399,10 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
   ctx->M = M;
   ctx->K = K;
   ctx->N = N;
+  const int wmode = recipe->no_2d_weights ? NVFP4_SCALE_1X16 : NVFP4_SCALE_16X16;
   set_shape(&ctx->xq, M, K, NVFP4_SCALE_1X16);
-  set_shape(&ctx->wq, N, K, NVFP4_SCALE_16X16);
-  set_shape(&ctx->wqt, K, N, NVFP4_SCALE_16X16);
+  set_shape(&ctx->wq, N, K, wmode);
+  set_shape(&ctx->wqt, K, N, wmode);
   NVFP4_HIP(zero_slots(workspace, kSlotXRaw, 3, s));
 
   // X: row-wise copy for Fprop and, when training, (R X)^T for Wgrad.
@@ -404,13 +415,15 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
   ax.status = ws_word(workspace, kSlotStatus);
   ax.row = copy_args(&ctx->xq, workspace, kSlotXRaw, nullptr);
   int fx = kFRow;
+  const bool x_rht = recipe->training && !recipe->no_rht;
   if (recipe->training) {
     set_shape(&ctx->xqt, K, M, NVFP4_SCALE_1X16);
-    ax.col = copy_args(&ctx->xqt, workspace, kSlotXRht, nullptr);
-    fx |= kFCol | kFRht;
+    // without the RHT the column copy has the row copy's amax
+    ax.col = copy_args(&ctx->xqt, workspace, x_rht ? kSlotXRht : kSlotXRaw, nullptr);
+    fx |= kFCol | (x_rht ? kFRht : 0);
   }
   NVFP4_HIP(launch_amax(x, dtype, M, K, K, recipe->rht_signs, ws_word(workspace, kSlotXRaw),
-                        recipe->training ? ws_word(workspace, kSlotXRht) : nullptr, s));
+                        x_rht ? ws_word(workspace, kSlotXRht) : nullptr, s));
   NVFP4_HIP(launch_quant_tile(dtype, fx, ax, s));
 
   // W: 16x16 scales, with the transposed copy for Dgrad.
@@ -423,7 +436,7 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
   aw.row = copy_args(&ctx->wq, workspace, kSlotW, nullptr);
   aw.col = copy_args(&ctx->wqt, workspace, kSlotW, nullptr);
   NVFP4_HIP(launch_amax(w, dtype, N, K, K, 0, ws_word(workspace, kSlotW), nullptr, s));
-  NVFP4_HIP(launch_quant_tile(dtype, kFRow | kFCol | kF2D, aw, s));
+  NVFP4_HIP(launch_quant_tile(dtype, kFRow | kFCol | (recipe->no_2d_weights ? 0 : kF2D), aw, s));
 
   // Fprop: Y = Q(X) Q(W)^T
   NVFP4_HIP(launch_gemm(gemm_operand(&ctx->xq), gemm_operand(&ctx->wq), K, y, kDtypeBF16, N, s));
@@ -461,13 +474,16 @@ nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* c
   ad.ld = N;
   ad.signs = recipe->rht_signs;
   ad.status = ws_word(workspace, kSlotStatus);
-  nvfp4_quant_opts o_row{NVFP4_SR, 0, 0, recipe->rht_signs, sr_seed, 0, 0};
-  nvfp4_quant_opts o_col{NVFP4_SR, 1, 1, recipe->rht_signs, sr_seed, 0, 1};
+  const bool rht = !recipe->no_rht, sr = !recipe->no_sr;
+  const int32_t rnd = sr ? NVFP4_SR : NVFP4_RN;
+  nvfp4_quant_opts o_row{rnd, 0, 0, recipe->rht_signs, sr_seed, 0, 0};
+  nvfp4_quant_opts o_col{rnd, 1, rht ? 1 : 0, recipe->rht_signs, sr_seed, 0, 1};
   ad.row = copy_args(&ctx->dyq, workspace, kSlotDyRaw, &o_row);
-  ad.col = copy_args(&ctx->dyqt, workspace, kSlotDyRht, &o_col);
+  ad.col = copy_args(&ctx->dyqt, workspace, rht ? kSlotDyRht : kSlotDyRaw, &o_col);
   NVFP4_HIP(launch_amax(dy, dtype, M, N, N, recipe->rht_signs, ws_word(workspace, kSlotDyRaw),
-                        ws_word(workspace, kSlotDyRht), s));
-  NVFP4_HIP(launch_quant_tile(dtype, kFRow | kFCol | kFRht | kFSrRow | kFSrCol, ad, s));
+                        rht ? ws_word(workspace, kSlotDyRht) : nullptr, s));
+  NVFP4_HIP(launch_quant_tile(
+      dtype, kFRow | kFCol | (rht ? kFRht : 0) | (sr ? kFSrRow | kFSrCol : 0), ad, s));
 
   // Dgrad: dX = Q(dY) Q(W^T)^T [M, K];  Wgrad: dW = Q((R dY)^T) Q((R X)^T)^T [N, K]
   // (one launch: the Wgrad tiles fill the Dgrad tail)

@@ -418,6 +418,59 @@ __global__ __launch_bounds__(kThreads) void rht16_axis1_kernel(const TIn* __rest
   for (int k = 0; k < 4; ++k) o[k] = make_float4(u[4 * k], u[4 * k + 1], u[4 * k + 2], u[4 * k + 3]);
 }
 
+// ---------------------------------------------------------------- dequantise
+
+// x_hat = e2m1(code) * d_b * g [Review s1 Step 3] (NVFP4 modes) or
+// e2m1(code) * 2^(s - 127) (MXFP4), in fp32: e2m1 * d_b is exact (at most 5
+// significant bits), so each output is the exact product rounded once.  One
+// thread per 8 consecutive elements of a row.  mode: 0 1x16, 1 16x16, 2 MX32.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ global,
+                                                      int64_t rows, int64_t cols, int mode,
+                                                      float* __restrict__ out, int64_t ldo) {
+  const int64_t per_row = cols / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * per_row) return;
+  const int64_t r = i / per_row, c = (i - r * per_row) * 8;
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * (cols / 2) + c / 2);
+  float d, g = 1.0f;  // out = (e2m1 * d) * g: the first product is exact
+  if (mode == 2) {
+    const uint32_t sc = scales[r * (cols / 32) + c / 32];
+    d = sc == 0xFFu ? __uint_as_float(0x7FC00000u)
+                    : (sc == 0u ? 0x1p-127f : __uint_as_float(sc << 23));  // 2^(sc-127)
+  } else {
+    const uint32_t sc = mode == 0 ? scales[r * (cols / 16) + c / 16]
+                                  : scales[(r / 16) * (cols / 16) + c / 16];
+    // fp16 bit pattern sc << 7 has the value d * 2^-8 for every E4M3 code
+    const uint16_t hb = (uint16_t)(sc << 7);
+    _Float16 hv;
+    __builtin_memcpy(&hv, &hb, 2);
+    d = (float)hv * 256.0f;
+    g = *global;
+  }
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  float v[8];
+  const float2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const float2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const float2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const float2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+  v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+  float4* o = reinterpret_cast<float4*>(out + r * ldo + c);
+  o[0] = make_float4(v[0] * d * g, v[1] * d * g, v[2] * d * g, v[3] * d * g);
+  o[1] = make_float4(v[4] * d * g, v[5] * d * g, v[6] * d * g, v[7] * d * g);
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* global,
+                          int64_t rows, int64_t cols, int mode, float* out, int64_t ldo,
+                          hipStream_t s) {
+  const int64_t n = rows * (cols / 8);
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes,
+                     scales, global, rows, cols, mode, out, ldo);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- MXFP4
 
 // MXFP4 comparator [Review "Core idea"; method summary s2]: one thread per

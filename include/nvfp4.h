@@ -116,17 +116,30 @@ typedef struct {
  * Fig. 5]: 16x16 weight scales, RHT on the Wgrad inputs only, stochastic
  * rounding on the gradient copies only.  The pages fix one sign seed for the
  * whole run: use nvfp4_rht_signs_from_seed(0) unless another is wanted. */
+/* The layer recipe.  All-zero switches give the pages' recipe [Review "Core
+ * idea" items (2)-(4); Captions Fig. 4]; each switch removes one component,
+ * as the pages' ablations do [Captions Fig. 4, 10, 11, 14]:
+ *   no_2d_weights  W and W^T are each quantised with 1x16 blocks along their
+ *                  own rows (W along K for Fprop, W^T along N for Dgrad), so
+ *                  the two copies differ (w_fprop != w_bprop) [Review s2]
+ *   no_rht         the Wgrad copies (X^T, dY^T) skip the RHT
+ *   no_sr          the dY copies round to nearest-even
+ * A backward must use the recipe of its forward. */
 typedef struct {
   uint32_t rht_signs;   /* sign diagonal shared by every RHT of the layer */
   int32_t training;     /* forward also builds the Wgrad copy of X */
+  int32_t no_2d_weights;
+  int32_t no_rht;
+  int32_t no_sr;
 } nvfp4_recipe;
 
 /* Buffers of one layer step Y = X W^T, X [M, K], W [N, K], dY [M, N].
  * The caller allocates each operand with nvfp4_tensor_bytes() and fills
  * codes/scales/global_scale pointers; shapes are set by the library.
  *   xq   X       [M, K] 1x16 RN          (Fprop A)
- *   wq   W       [N, K] 16x16 RN         (Fprop B)
+ *   wq   W       [N, K] 16x16 RN         (Fprop B)      (1x16 with no_2d_weights)
  *   wqt  W^T     [K, N] 16x16 RN, same codes transposed, same g (Dgrad B)
+ *                (no_2d_weights: W^T quantised on its own, 1x16 along N, same g)
  *   xqt  (R X)^T [K, M] 1x16 along tokens, RHT, RN              (Wgrad B)
  *   dyq  dY      [M, N] 1x16 SR, stream 0                       (Dgrad A)
  *   dyqt (R dY)^T [N, M] 1x16 along tokens, RHT, SR, stream 1   (Wgrad A) */
@@ -199,6 +212,15 @@ nvfp4_status nvfp4_quantize_rowcol(const void* x, int32_t dtype, int64_t rows, i
 nvfp4_status nvfp4_quantize_2d(const void* w, int32_t dtype, int64_t rows, int64_t cols,
                                int64_t ld, nvfp4_tensor* out, nvfp4_tensor* out_t,
                                void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_dequantize: decode an operand [Review s1 Step 3]: out[r][c] =
+ * e2m1(code) * d_b * g for the 1x16 and 16x16 modes, e2m1(code) * 2^(s - 127)
+ * for NVFP4_SCALE_MX32 (E8M0 code 0xFF decodes to NaN), in fp32 (e2m1 * d_b
+ * is exact, so each value is the exact product rounded once).  out: fp32
+ * [rows][ldo], ldo >= cols and a multiple of 4, 16-byte aligned.
+ */
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor* t, float* out, int64_t ldo, void* stream);
 
 /*
  * nvfp4_mx_quantize: MXFP4 quantisation of x [rows, cols] (leading dim ld,

@@ -296,9 +296,15 @@ def dequant_rows(q: QTensor, rows) -> np.ndarray:
 class Recipe:
     """The pages' training recipe for one linear layer [Review "Core idea"]:
     16x16 weight scales, RHT on the Wgrad inputs only, stochastic rounding on
-    the gradient copies only."""
+    the gradient copies only.  Each switch removes one component, as the
+    pages' ablations do [Captions Fig. 4, 10, 11, 14]: weights_2d=False
+    quantises W (1x16 along K) and W^T (1x16 along N) separately, rht=False
+    drops the RHT from the Wgrad copies, sr=False rounds dY to nearest."""
     rht_signs: int
     sr_seed: int = 1234
+    weights_2d: bool = True
+    rht: bool = True
+    sr: bool = True
 
 
 def linear_operands(x, w, dy, recipe: Recipe):
@@ -314,11 +320,15 @@ def linear_operands(x, w, dy, recipe: Recipe):
     s = recipe.rht_signs
     ops = {}
     ops["xq"] = quantize(x)
-    ops["wq"], ops["wqt"] = quantize_2d(w)
-    ops["xqt"] = quantize(x, transpose=True, rht=True, signs=s)
+    if recipe.weights_2d:
+        ops["wq"], ops["wqt"] = quantize_2d(w)
+    else:
+        ops["wq"] = quantize(w)
+        ops["wqt"] = quantize(w, transpose=True)
+    ops["xqt"] = quantize(x, transpose=True, rht=recipe.rht, signs=s)
     if dy is not None:
-        ops["dyq"] = quantize(dy, sr=True, seed=recipe.sr_seed, stream=0)
-        ops["dyqt"] = quantize(dy, transpose=True, rht=True, signs=s, sr=True,
+        ops["dyq"] = quantize(dy, sr=recipe.sr, seed=recipe.sr_seed, stream=0)
+        ops["dyqt"] = quantize(dy, transpose=True, rht=recipe.rht, signs=s, sr=recipe.sr,
                                seed=recipe.sr_seed, stream=1)
     return ops
 

@@ -122,6 +122,17 @@ def test_mx_argument_errors():
     assert (cb, sb) == (64 * 48, 64 * 3)
 
 
+def test_dequantize_argument_errors():
+    f = nv._lib.nvfp4_dequantize
+    t = nv.c_tensor(P, P, P, 64, 256, nv.SCALE_1X16)
+    assert f(ctypes.byref(t), None, 256, None) == nv.ERR_NULL
+    assert f(ctypes.byref(t), P, 200, None) == nv.ERR_SHAPE       # ldo < cols
+    assert f(ctypes.byref(t), P, 258, None) == nv.ERR_SHAPE       # ldo % 4
+    assert f(ctypes.byref(t), P + 4, 256, None) == nv.ERR_ALIGN
+    no_g = nv.c_tensor(P, P, None, 64, 256, nv.SCALE_1X16)       # NVFP4 needs g
+    assert f(ctypes.byref(no_g), P, 256, None) == nv.ERR_NULL
+
+
 def test_2d_rht_and_layer_argument_errors():
     t = _tensor()
     assert nv._lib.nvfp4_quantize_2d(P, nv.BF16, 40, 32, 32, ctypes.byref(t), None, P, WSB,
