@@ -78,6 +78,10 @@ def lib():
         L.oracle_e2m1_sr_index_n.argtypes = [f32p, u32p, i64, u8p]
         L.oracle_sr_bits_n.restype = None
         L.oracle_sr_bits_n.argtypes = [u64, u32, u64, i64, u32p]
+        L.oracle_rht_signs128_from_seed.restype = None
+        L.oracle_rht_signs128_from_seed.argtypes = [u64, u32p]
+        L.oracle_rht_d.restype = i32
+        L.oracle_rht_d.argtypes = [f32p, i64, i64, i64, i32, i32, u32p, f32p]
         L.oracle_mx_block.restype = ctypes.c_uint8
         L.oracle_mx_block.argtypes = [f32p, i32, u8p]
         L.oracle_mx_quantize.restype = i32
@@ -392,3 +396,28 @@ def mx_gemm(a: MXTensor, b: MXTensor):
     operands) and S = |deq(A)| |deq(B)|^T for the tolerance."""
     ah, bh = mx_dequant(a), mx_dequant(b)
     return ah @ bh.T, np.abs(ah) @ np.abs(bh).T
+
+
+# ---------------------------------------------------------------- RHT sizes
+# [Review s3 size note; Captions Fig. 12]: d = 4, 16 (the recipe), 128.
+
+
+def rht_signs128_from_seed(seed: int) -> np.ndarray:
+    """The 128 sign bits (4 words, word 0 first, LSB first) from a seed; the
+    low 16 bits of word 0 are rht_signs_from_seed(seed)."""
+    out = np.zeros(4, np.uint32)
+    lib().oracle_rht_signs128_from_seed(seed, out)
+    return out
+
+
+def rht(x, axis: int, d: int, signs) -> np.ndarray:
+    """y = fp32(1/sqrt(d)) H_d diag(s) x on every d-element chunk along
+    `axis` (1: rows, 0: columns); signs = 4 words of sign bits."""
+    x = _f32(x)
+    R, C = x.shape
+    y = np.empty((R, C), np.float32)
+    sg = np.ascontiguousarray(np.asarray(signs, np.uint32).reshape(4))
+    st = lib().oracle_rht_d(x, R, C, C, axis, d, sg, y)
+    if st:
+        raise OracleError(st)
+    return y

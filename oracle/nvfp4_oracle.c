@@ -588,3 +588,59 @@ void oracle_mx_dequant(const uint8_t* codes, const uint8_t* scales, int64_t R, i
       out[i * C + j] = oracle_e2m1_decode(code) * oracle_e8m0_decode(scales[i * (C / 32) + j / 32]);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Random Hadamard transforms of other sizes [Review s3 and its size note:  */
+/* d = 16 is the recipe, d = 4 and d = 128 the sizes the pages compare it   */
+/* against; Captions Fig. 12].  y = c * H_d * diag(s) * x per d-element     */
+/* chunk, H_d Sylvester, c = fp32(1/sqrt(d)) (orthonormal; exact for d = 4  */
+/* and 16).  fp32 order as for d = 16: signs, butterflies h = 1, 2, ...,    */
+/* d/2 as (a+b, a-b), then x c.  Signs: bit i of the 128-bit Philox4x32-10  */
+/* block (counter 0, key = seed), word 0 first, least significant bit      */
+/* first -- the low 16 bits are exactly the d = 16 mask above.               */
+/* ------------------------------------------------------------------------ */
+void oracle_rht_signs128_from_seed(uint64_t seed, uint32_t out[4]) {
+  const uint32_t ctr[4] = {0u, 0u, 0u, 0u};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  oracle_philox4x32_10(ctr, key, out);
+}
+
+void oracle_rht_chunk_d(const float* x, int d, const uint32_t signs[4], float* y) {
+  float u[128];
+  for (int i = 0; i < d; ++i) u[i] = ((signs[i / 32] >> (i % 32)) & 1u) ? -x[i] : x[i];
+  for (int h = 1; h < d; h *= 2) {
+    for (int i = 0; i < d; ++i) {
+      if (i & h) continue;
+      float a = u[i], b = u[i + h];
+      u[i] = a + b;
+      u[i + h] = a - b;
+    }
+  }
+  const float c = (float)(1.0 / sqrt((double)d));
+  for (int i = 0; i < d; ++i) y[i] = u[i] * c;
+}
+
+/* RHT of size d (4, 16 or 128) of a [rows, cols] fp32 matrix: axis 1 chunks
+ * along each row, axis 0 along each column; output dense [rows, cols]. */
+int oracle_rht_d(const float* x, int64_t rows, int64_t cols, int64_t ld, int axis, int d,
+                 const uint32_t signs[4], float* y) {
+  if (d != 4 && d != 16 && d != 128) return ORACLE_ERR_SHAPE;
+  if (axis == 1) {
+    if (cols % d) return ORACLE_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+      for (int64_t c = 0; c < cols; c += d) oracle_rht_chunk_d(x + r * ld + c, d, signs, y + r * cols + c);
+  } else {
+    if (rows % d) return ORACLE_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; ++c) {
+      for (int64_t r = 0; r < rows; r += d) {
+        float in[128], out[128];
+        for (int i = 0; i < d; ++i) in[i] = x[(r + i) * ld + c];
+        oracle_rht_chunk_d(in, d, signs, out);
+        for (int i = 0; i < d; ++i) y[(r + i) * cols + c] = out[i];
+      }
+    }
+  }
+  return ORACLE_OK;
+}
