@@ -111,6 +111,39 @@ def cpu_baseline(sample_tokens: int):
     }
 
 
+def rht_sizes(nv, x, ws, reps: int):
+    """The Wgrad copy of X, (R_d X)^T quantised along tokens, at the layer's
+    shape: d = 16 fused into the quantiser (the recipe), d = 4 and 128 as
+    nvfp4_rht followed by nvfp4_quantize of the transpose (HIP events)."""
+    import torch
+    signs16 = nv.nvfp4_rht_signs_from_seed(0)
+    signs = nv.nvfp4_rht_signs128_from_seed(0)
+    y = torch.empty(M, K, dtype=torch.float32, device=x.device)
+    q = nv.nvfp4_quantize(x, ws, transpose=True, rht=True, rht_signs=signs16)
+
+    def d16():
+        nv.nvfp4_quantize(x, ws, q, transpose=True, rht=True, rht_signs=signs16)
+
+    def dd(d):
+        def f():
+            nv.nvfp4_rht(x, 0, d, signs, y)
+            nv.nvfp4_quantize(y, ws, q, transpose=True)
+        return f
+
+    out = {"workload": f"(R_d X)^T, X [{M}, {K}] bf16, quantised along tokens"}
+    stream = torch.cuda.current_stream()
+    for name, f in (("d16_fused_ms", d16), ("d4_ms", dd(4)), ("d128_ms", dd(128))):
+        f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / reps, 4)
+    return out
+
+
 def weight_consistency(nv, w, ws):
     """w_fprop vs w_bprop [Review s2; Captions Fig. 14]: relative Frobenius
     difference between the decoded Fprop copy of W and the decoded Dgrad copy
@@ -266,6 +299,7 @@ def main():
     }
     out["mxfp4_comparator"] = mxfp4_comparator(nv, x, w, max(3, args.steps // 2))
     out["weight_consistency"] = weight_consistency(nv, w, ws)
+    out["rht_sizes"] = rht_sizes(nv, x, ws, max(3, args.steps // 2))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

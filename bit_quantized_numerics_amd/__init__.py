@@ -75,6 +75,8 @@ _SIGS = {
     "nvfp4_rht16": (_i32, [_vp, _vp, _i32, _i64, _i64, _i64, _i32, _u32, _vp]),
     "nvfp4_mx_quantize": (_i32, [_vp, _i32, _i64, _i64, _i64, _T, _vp]),
     "nvfp4_dequantize": (_i32, [_T, _vp, _i64, _vp]),
+    "nvfp4_rht": (_i32, [_vp, _vp, _i32, _i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_u32), _vp]),
+    "nvfp4_rht_signs128_from_seed": (None, [_u64, ctypes.POINTER(_u32)]),
     "nvfp4_gemm": (_i32, [_T, _T, _vp, _i32, _i64, _vp, _sz, _vp]),
     "nvfp4_linear_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.POINTER(c_recipe),
                                 ctypes.POINTER(c_linear_ctx), _vp, _sz, _vp]),
@@ -256,6 +258,23 @@ def nvfp4_rht16(x: torch.Tensor, axis: int, rht_signs: int, y: torch.Tensor | No
     _check(_lib.nvfp4_rht16(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
                             _dtype_code(x), rows, cols, _ld(x), axis, rht_signs, _stream(x.device)),
            "nvfp4_rht16")
+    return y
+
+
+def nvfp4_rht_signs128_from_seed(seed: int) -> tuple:
+    out = (_u32 * 4)()
+    _lib.nvfp4_rht_signs128_from_seed(seed, out)
+    return tuple(out)
+
+
+def nvfp4_rht(x: torch.Tensor, axis: int, d: int, signs, y: torch.Tensor | None = None):
+    """Hadamard transform of size d (4, 16, 128) along axis; signs: 4 words."""
+    rows, cols = x.shape
+    if y is None:
+        y = torch.empty(rows, cols, dtype=torch.float32, device=x.device)
+    sg = (_u32 * 4)(*[int(v) for v in signs])
+    _check(_lib.nvfp4_rht(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()), _dtype_code(x),
+                          rows, cols, _ld(x), axis, d, sg, _stream(x.device)), "nvfp4_rht")
     return y
 
 

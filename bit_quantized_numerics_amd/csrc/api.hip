@@ -11,6 +11,8 @@
 
 #include "internal.h"
 
+#include <cmath>
+
 namespace {
 
 using namespace nvfp4;
@@ -181,6 +183,17 @@ uint32_t nvfp4_rht_signs_from_seed(uint64_t seed) {
   return c[0] & 0xFFFFu;
 }
 
+void nvfp4_rht_signs128_from_seed(uint64_t seed, uint32_t* out) {
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  philox_host(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  if (out) {
+    out[0] = c[0];
+    out[1] = c[1];
+    out[2] = c[2];
+    out[3] = c[3];
+  }
+}
+
 nvfp4_status nvfp4_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
   NVFP4_TRY(check_workspace(workspace, ws_bytes));
   NVFP4_HIP(launch_zero_words(static_cast<uint32_t*>(workspace), kWsWords, as_stream(stream)));
@@ -329,6 +342,23 @@ nvfp4_status nvfp4_rht16(const void* x, float* y, int32_t in_dtype, int64_t rows
   if (!aligned(x, 16) || !aligned(y, 16) || (ld * (int64_t)elem_bytes(in_dtype)) % 16 != 0)
     return NVFP4_ERR_ALIGN;
   NVFP4_HIP(launch_rht16(x, y, in_dtype, rows, cols, ld, axis, rht_signs, as_stream(stream)));
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_rht(const void* x, float* y, int32_t in_dtype, int64_t rows, int64_t cols,
+                       int64_t ld, int32_t axis, int32_t d, const uint32_t* signs, void* stream) {
+  if (!x || !y || !signs) return NVFP4_ERR_NULL;
+  if (d != 4 && d != 16 && d != 128) return NVFP4_ERR_SHAPE;
+  if (d == 16) return nvfp4_rht16(x, y, in_dtype, rows, cols, ld, axis, signs[0] & 0xFFFFu, stream);
+  if (in_dtype != NVFP4_F32 && in_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  if (axis != 0 && axis != 1) return NVFP4_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || ld < cols) return NVFP4_ERR_SHAPE;
+  if (axis == 1 && cols % (d < 8 ? 8 : d) != 0) return NVFP4_ERR_SHAPE;
+  if (axis == 0 && rows % d != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 16) || (ld * (int64_t)elem_bytes(in_dtype)) % 16 != 0)
+    return NVFP4_ERR_ALIGN;
+  const float c = (float)(1.0 / std::sqrt((double)d));
+  NVFP4_HIP(launch_rht_d(x, y, in_dtype, rows, cols, ld, axis, d, signs, c, as_stream(stream)));
   return NVFP4_OK;
 }
 

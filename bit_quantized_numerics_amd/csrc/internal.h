@@ -45,6 +45,8 @@ hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t s);
 hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                        uint32_t signs, uint32_t* out_raw, uint32_t* out_rht, hipStream_t s);
 hipError_t launch_quant_tile(int dtype, int flags, const TileArgs& a, hipStream_t s);
+hipError_t launch_rht_d(const void* x, float* y, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                        int axis, int d, const uint32_t* signs, float c, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* global,
                           int64_t rows, int64_t cols, int mode, float* out, int64_t ldo,
                           hipStream_t s);

@@ -418,6 +418,96 @@ __global__ __launch_bounds__(kThreads) void rht16_axis1_kernel(const TIn* __rest
   for (int k = 0; k < 4; ++k) o[k] = make_float4(u[4 * k], u[4 * k + 1], u[4 * k + 2], u[4 * k + 3]);
 }
 
+// Hadamard transform of size D (4 or 128) [Review s3 size note; Captions
+// Fig. 12]: y = c H_D diag(s) x per D-element chunk, signs first, butterflies
+// h = 1 .. D/2 as (a+b, a-b), then x c (c = fp32(1/sqrt(D)), passed in).
+// Sign bit i is bit i % 32 of sg[i / 32].
+template <int D>
+__device__ __forceinline__ void rht_d_inplace(float* u, const uint32_t (&sg)[4], float c) {
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if ((sg[i / 32] >> (i % 32)) & 1u) u[i] = -u[i];
+#pragma unroll
+  for (int h = 1; h < D; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (i & h) continue;
+      const float a = u[i], b = u[i + h];
+      u[i] = a + b;
+      u[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < D; ++i) u[i] = u[i] * c;
+}
+
+__device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+
+// axis 0: thread = one column's D-row chunk (lanes on consecutive columns, so
+// each row access of a wave is contiguous).  axis 1: thread = 8 consecutive
+// elements of a row (D = 4: two chunks) or one 128-element chunk.
+template <typename TIn, int D, int AXIS>
+__global__ __launch_bounds__(256) void rht_d_kernel(const TIn* __restrict__ x, float* __restrict__ y,
+                                                    int64_t rows, int64_t cols, int64_t ld,
+                                                    uint32_t s0, uint32_t s1, uint32_t s2,
+                                                    uint32_t s3, float c) {
+  const uint32_t sg[4] = {s0, s1, s2, s3};
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (AXIS == 0) {
+    if (idx >= (rows / D) * cols) return;
+    const int64_t col = idx % cols, r0 = (idx / cols) * D;
+    float u[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) u[i] = load1(x + (r0 + i) * ld + col);
+    rht_d_inplace<D>(u, sg, c);
+#pragma unroll
+    for (int i = 0; i < D; ++i) y[(r0 + i) * cols + col] = u[i];
+  } else {
+    constexpr int E = D < 8 ? 8 : D;  // elements per thread
+    const int64_t per_row = cols / E;
+    if (idx >= rows * per_row) return;
+    const int64_t r = idx / per_row, c0 = (idx - r * per_row) * E;
+    float u[E];
+#pragma unroll
+    for (int q = 0; q < E / 8; ++q) load8(x + r * ld + c0 + 8 * q, u + 8 * q);
+#pragma unroll
+    for (int q = 0; q < E / D; ++q) rht_d_inplace<D>(u + q * D, sg, c);
+    float4* o = reinterpret_cast<float4*>(y + r * cols + c0);
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) o[q] = make_float4(u[4 * q], u[4 * q + 1], u[4 * q + 2], u[4 * q + 3]);
+  }
+}
+
+template <typename TIn, int D>
+static void launch_rht_d_t(const void* x, float* y, int64_t rows, int64_t cols, int64_t ld,
+                           int axis, const uint32_t* sg, float c, hipStream_t s) {
+  const TIn* p = static_cast<const TIn*>(x);
+  if (axis == 0) {
+    const int64_t n = (rows / D) * cols;
+    hipLaunchKernelGGL((rht_d_kernel<TIn, D, 0>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       p, y, rows, cols, ld, sg[0], sg[1], sg[2], sg[3], c);
+  } else {
+    const int64_t n = rows * (cols / (D < 8 ? 8 : D));
+    hipLaunchKernelGGL((rht_d_kernel<TIn, D, 1>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       p, y, rows, cols, ld, sg[0], sg[1], sg[2], sg[3], c);
+  }
+}
+
+hipError_t launch_rht_d(const void* x, float* y, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                        int axis, int d, const uint32_t* signs, float c, hipStream_t s) {
+  if (d == 4) {
+    if (dtype == kDtypeBF16) launch_rht_d_t<uint16_t, 4>(x, y, rows, cols, ld, axis, signs, c, s);
+    else launch_rht_d_t<float, 4>(x, y, rows, cols, ld, axis, signs, c, s);
+  } else if (d == 128) {
+    if (dtype == kDtypeBF16) launch_rht_d_t<uint16_t, 128>(x, y, rows, cols, ld, axis, signs, c, s);
+    else launch_rht_d_t<float, 128>(x, y, rows, cols, ld, axis, signs, c, s);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- dequantise
 
 // x_hat = e2m1(code) * d_b * g [Review s1 Step 3] (NVFP4 modes) or

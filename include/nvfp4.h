@@ -214,6 +214,28 @@ nvfp4_status nvfp4_quantize_2d(const void* w, int32_t dtype, int64_t rows, int64
                                void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * nvfp4_rht: random Hadamard transform of size d = 4, 16 or 128 [Review s3
+ * and its size note: d = 16 is the recipe, 4 and 128 the sizes compared with
+ * it; Captions Fig. 12]: y = c * H_d * diag(s) * x per d-element chunk along
+ * `axis` (1: rows, cols % d == 0 (cols % 8 for d = 4); 0: columns,
+ * rows % d == 0), c = fp32(1/sqrt(d)) (exact for 4 and 16), fp32 order signs,
+ * butterflies h = 1 .. d/2 as (a+b, a-b), then x c.  signs: HOST array of 4
+ * words; sign bit i = bit i % 32 of signs[i / 32] (d = 16 uses the low 16
+ * bits of signs[0], exactly nvfp4_rht16).  y: dense fp32 [rows, cols].  A
+ * Wgrad operand with another size is nvfp4_rht(axis 0) followed by
+ * nvfp4_quantize(transpose 1) of y.  Sign options [Captions Fig. 13]: all
+ * zero (no randomisation), one seed for every layer, or a seed per layer via
+ * nvfp4_rht_signs128_from_seed.
+ */
+nvfp4_status nvfp4_rht(const void* x, float* y, int32_t in_dtype, int64_t rows, int64_t cols,
+                       int64_t ld, int32_t axis, int32_t d, const uint32_t* signs, void* stream);
+
+/* Host-side: the 128 sign bits from a seed = the Philox4x32-10 block
+ * (counter 0, key = seed), word 0 first; its low 16 bits are
+ * nvfp4_rht_signs_from_seed(seed).  out: 4 words. */
+void nvfp4_rht_signs128_from_seed(uint64_t seed, uint32_t* out);
+
+/*
  * nvfp4_dequantize: decode an operand [Review s1 Step 3]: out[r][c] =
  * e2m1(code) * d_b * g for the 1x16 and 16x16 modes, e2m1(code) * 2^(s - 127)
  * for NVFP4_SCALE_MX32 (E8M0 code 0xFF decodes to NaN), in fp32 (e2m1 * d_b

@@ -133,6 +133,19 @@ def test_dequantize_argument_errors():
     assert f(ctypes.byref(no_g), P, 256, None) == nv.ERR_NULL
 
 
+def test_rht_sizes_argument_errors():
+    f = nv._lib.nvfp4_rht
+    sg = (ctypes.c_uint32 * 4)(0, 0, 0, 0)
+    assert f(P, P, nv.BF16, 256, 256, 256, 0, 8, sg, None) == nv.ERR_SHAPE    # d
+    assert f(P, P, nv.BF16, 200, 256, 256, 0, 128, sg, None) == nv.ERR_SHAPE  # rows % d
+    assert f(P, P, nv.BF16, 256, 100, 100, 1, 4, sg, None) == nv.ERR_SHAPE    # cols % 8
+    assert f(P, P, nv.BF16, 256, 256, 256, 0, 128, None, None) == nv.ERR_NULL
+    assert f(P, P, 5, 256, 256, 256, 0, 128, sg, None) == nv.ERR_DTYPE
+    out = (ctypes.c_uint32 * 4)()
+    nv._lib.nvfp4_rht_signs128_from_seed(0, out)
+    assert out[0] & 0xFFFF == nv.nvfp4_rht_signs_from_seed(0)
+
+
 def test_2d_rht_and_layer_argument_errors():
     t = _tensor()
     assert nv._lib.nvfp4_quantize_2d(P, nv.BF16, 40, 32, 32, ctypes.byref(t), None, P, WSB,
