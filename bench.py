@@ -197,13 +197,45 @@ def mxfp4_comparator(nv, x, w, reps: int):
             "frac": round(tflops / PEAK_FP4_TFLOPS, 4)}
 
 
+def bf16_fprop(nv, x, w, ctx, ws, signs, reps: int):
+    """The precision switch's forward [Review s9; Captions Fig. 7] on the
+    Fprop shape: the plain BF16 GEMM alone, and the training forward with
+    bf16_fprop (backward copies of X and W, then the BF16 GEMM) next to the
+    NVFP4 training forward, timed with HIP events on the launch stream."""
+    import torch
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    runs = [lambda: nv.nvfp4_bf16_gemm(x, w, c=y),
+            lambda: nv.nvfp4_linear_fwd(x, w, ctx, ws, signs, training=True, y=y, bf16_fprop=True),
+            lambda: nv.nvfp4_linear_fwd(x, w, ctx, ws, signs, training=True, y=y)]
+    for _ in range(2):
+        for f in runs:
+            f()
+    stream = torch.cuda.current_stream()
+    tot = [0.0] * len(runs)
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(runs) + 1)]
+        ev[0].record(stream)
+        for i, f in enumerate(runs):
+            f()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        for i in range(len(runs)):
+            tot[i] += ev[i].elapsed_time(ev[i + 1])
+    tg, tf, tn = (t / reps for t in tot)
+    tflops = 2.0 * M * N * K / (tg * 1e-3) / 1e12
+    return {"workload": f"Fprop {M}x{K} by {N}x{K} in BF16 (no quantisation), bf16 out",
+            "gemm_ms": round(tg, 4), "gemm_TFLOPs": round(tflops, 1),
+            "peak_bf16_TFLOPs": PEAK_F16_TFLOPS, "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+            "layer_fwd_bf16_fprop_ms": round(tf, 4), "layer_fwd_nvfp4_ms": round(tn, 4)}
+
+
 def main():
     args = parse()
     if args.copy_mib:
         copy_reference(args.copy_mib)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
@@ -300,6 +332,7 @@ def main():
     out["mxfp4_comparator"] = mxfp4_comparator(nv, x, w, max(3, args.steps // 2))
     out["weight_consistency"] = weight_consistency(nv, w, ws)
     out["rht_sizes"] = rht_sizes(nv, x, ws, max(3, args.steps // 2))
+    out["bf16_fprop"] = bf16_fprop(nv, x, w, ctx, ws, signs, max(3, args.steps // 2))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

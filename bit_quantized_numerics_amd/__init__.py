@@ -48,7 +48,7 @@ class c_quant_opts(ctypes.Structure):
 class c_recipe(ctypes.Structure):
     _fields_ = [("rht_signs", ctypes.c_uint32), ("training", ctypes.c_int32),
                 ("no_2d_weights", ctypes.c_int32), ("no_rht", ctypes.c_int32),
-                ("no_sr", ctypes.c_int32)]
+                ("no_sr", ctypes.c_int32), ("bf16_fprop", ctypes.c_int32)]
 
 
 class c_linear_ctx(ctypes.Structure):
@@ -78,6 +78,7 @@ _SIGS = {
     "nvfp4_rht": (_i32, [_vp, _vp, _i32, _i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_u32), _vp]),
     "nvfp4_rht_signs128_from_seed": (None, [_u64, ctypes.POINTER(_u32)]),
     "nvfp4_gemm": (_i32, [_T, _T, _vp, _i32, _i64, _vp, _sz, _vp]),
+    "nvfp4_bf16_gemm": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
     "nvfp4_linear_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.POINTER(c_recipe),
                                 ctypes.POINTER(c_linear_ctx), _vp, _sz, _vp]),
     "nvfp4_linear_bwd": (_i32, [_vp, _i32, ctypes.POINTER(c_linear_ctx), _vp, _vp, _i32, _u64,
@@ -311,6 +312,25 @@ def nvfp4_gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, c: torch
     return c
 
 
+def nvfp4_bf16_gemm(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.float32,
+                    c: torch.Tensor | None = None):
+    """C = A B^T for dense bf16 A [M, K], B [N, K] (FP32 accumulation)."""
+    if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise NVFP4Error(ERR_DTYPE, "nvfp4_bf16_gemm: operands must be bfloat16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise NVFP4Error(ERR_SHAPE, "nvfp4_bf16_gemm: shapes")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise NVFP4Error(ERR_ALIGN, "nvfp4_bf16_gemm: operands must be dense row-major")
+    M, K = a.shape
+    N = b.shape[0]
+    if c is None:
+        c = torch.empty(M, N, dtype=out_dtype, device=a.device)
+    _check(_lib.nvfp4_bf16_gemm(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                ctypes.c_void_p(c.data_ptr()), M, N, K, _dtype_code(c), _ld(c),
+                                _stream(a.device)), "nvfp4_bf16_gemm")
+    return c
+
+
 class LinearContext:
     """Caller-owned quantised operands of one layer step (Y = X W^T)."""
 
@@ -331,18 +351,20 @@ class LinearContext:
             getattr(self, name).update(getattr(self.cctx, name))
 
 
-def _recipe(rht_signs, training, no_2d_weights, no_rht, no_sr):
-    return c_recipe(int(rht_signs), int(training), int(no_2d_weights), int(no_rht), int(no_sr))
+def _recipe(rht_signs, training, no_2d_weights, no_rht, no_sr, bf16_fprop=False):
+    return c_recipe(int(rht_signs), int(training), int(no_2d_weights), int(no_rht), int(no_sr),
+                    int(bf16_fprop))
 
 
 def nvfp4_linear_fwd(x: torch.Tensor, w: torch.Tensor, ctx: LinearContext, ws: Workspace,
                      rht_signs: int, training: bool = True, y: torch.Tensor | None = None, *,
-                     no_2d_weights: bool = False, no_rht: bool = False, no_sr: bool = False):
+                     no_2d_weights: bool = False, no_rht: bool = False, no_sr: bool = False,
+                     bf16_fprop: bool = False):
     M, K = x.shape
     N = w.shape[0]
     if y is None:
         y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
-    rec = _recipe(rht_signs, training, no_2d_weights, no_rht, no_sr)
+    rec = _recipe(rht_signs, training, no_2d_weights, no_rht, no_sr, bf16_fprop)
     _check(_lib.nvfp4_linear_fwd(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
                                  ctypes.c_void_p(y.data_ptr()), M, K, N, _dtype_code(x),
                                  ctypes.byref(rec), ctypes.byref(ctx.cctx), ws.ptr, ws.nbytes,

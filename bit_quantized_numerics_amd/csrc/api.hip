@@ -66,6 +66,15 @@ nvfp4_status check_source(const void* x, int32_t dtype, int64_t rows, int64_t co
   return NVFP4_OK;
 }
 
+// A dense bf16 GEMM operand [rows, K]: K a whole number of 32-wide slabs and
+// at least three of them (the kernel's prologue loads three), and every
+// 256-row tile addressable with 32-bit buffer offsets.
+nvfp4_status check_bf16_operand(int64_t rows, int64_t K) {
+  if (rows <= 0 || K < 96 || K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if ((rows + 255) / 256 * 256 * K * 2 >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
 nvfp4_status check_out(const nvfp4_tensor* t) {
   if (!t || !t->codes || !t->scales || !t->global_scale) return NVFP4_ERR_NULL;
   if (!aligned(t->codes, 16) || !aligned(t->global_scale, 4)) return NVFP4_ERR_ALIGN;
@@ -411,17 +420,42 @@ nvfp4_status nvfp4_mx_quantize(const void* x, int32_t dtype, int64_t rows, int64
   return NVFP4_OK;
 }
 
+nvfp4_status nvfp4_bf16_gemm(const void* a, const void* b, void* c, int64_t M, int64_t N,
+                             int64_t K, int32_t c_dtype, int64_t ldc, void* stream) {
+  if (!a || !b || !c) return NVFP4_ERR_NULL;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  NVFP4_TRY(check_bf16_operand(M, K));
+  NVFP4_TRY(check_bf16_operand(N, K));
+  if (ldc < N) return NVFP4_ERR_SHAPE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, elem_bytes(c_dtype)))
+    return NVFP4_ERR_ALIGN;
+  NVFP4_HIP(launch_bf16_gemm(a, M, b, N, K, c, c_dtype == NVFP4_BF16 ? kDtypeBF16 : kDtypeF32, ldc,
+                             as_stream(stream)));
+  return NVFP4_OK;
+}
+
 nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, int64_t K, int64_t N,
                               int32_t dtype, const nvfp4_recipe* recipe, nvfp4_linear_ctx* ctx,
                               void* workspace, size_t ws_bytes, void* stream) {
   if (!recipe || !ctx || !y) return NVFP4_ERR_NULL;
   if (M % 16 || K % 16 || N % 16) return NVFP4_ERR_SHAPE;
+  const bool bf16_fprop = recipe->bf16_fprop != 0;
   NVFP4_TRY(check_source(x, dtype, M, K, K));
   NVFP4_TRY(check_source(w, dtype, N, K, K));
-  NVFP4_TRY(check_out(&ctx->xq));
-  NVFP4_TRY(check_out(&ctx->wq));
-  NVFP4_TRY(check_out(&ctx->wqt));
-  if (recipe->training) NVFP4_TRY(check_out(&ctx->xqt));
+  if (bf16_fprop) {
+    if (dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+    NVFP4_TRY(check_bf16_operand(M, K));
+    NVFP4_TRY(check_bf16_operand(N, K));
+  } else {
+    NVFP4_TRY(check_out(&ctx->xq));
+    NVFP4_TRY(check_out(&ctx->wq));
+  }
+  if (recipe->training) {
+    NVFP4_TRY(check_out(&ctx->wqt));
+    NVFP4_TRY(check_out(&ctx->xqt));
+  } else if (!bf16_fprop) {
+    NVFP4_TRY(check_out(&ctx->wqt));
+  }
   if (recipe->rht_signs > 0xFFFFu) return NVFP4_ERR_DTYPE;
   NVFP4_TRY(check_workspace(workspace, ws_bytes));
   if (!aligned(y, 4)) return NVFP4_ERR_ALIGN;
@@ -430,9 +464,13 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
   ctx->K = K;
   ctx->N = N;
   const int wmode = recipe->no_2d_weights ? NVFP4_SCALE_1X16 : NVFP4_SCALE_16X16;
-  set_shape(&ctx->xq, M, K, NVFP4_SCALE_1X16);
-  set_shape(&ctx->wq, N, K, wmode);
-  set_shape(&ctx->wqt, K, N, wmode);
+  if (!bf16_fprop) {
+    set_shape(&ctx->xq, M, K, NVFP4_SCALE_1X16);
+    set_shape(&ctx->wq, N, K, wmode);
+  }
+  // The BF16 forward of an inference call quantises nothing.
+  const bool want_wt = recipe->training || !bf16_fprop;
+  if (want_wt) set_shape(&ctx->wqt, K, N, wmode);
   NVFP4_HIP(zero_slots(workspace, kSlotXRaw, 3, s));
 
   // X: row-wise copy for Fprop and, when training, (R X)^T for Wgrad.
@@ -443,8 +481,11 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
   ax.ld = K;
   ax.signs = recipe->rht_signs;
   ax.status = ws_word(workspace, kSlotStatus);
-  ax.row = copy_args(&ctx->xq, workspace, kSlotXRaw, nullptr);
-  int fx = kFRow;
+  int fx = 0;
+  if (!bf16_fprop) {
+    ax.row = copy_args(&ctx->xq, workspace, kSlotXRaw, nullptr);
+    fx |= kFRow;
+  }
   const bool x_rht = recipe->training && !recipe->no_rht;
   if (recipe->training) {
     set_shape(&ctx->xqt, K, M, NVFP4_SCALE_1X16);
@@ -452,24 +493,35 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
     ax.col = copy_args(&ctx->xqt, workspace, x_rht ? kSlotXRht : kSlotXRaw, nullptr);
     fx |= kFCol | (x_rht ? kFRht : 0);
   }
-  NVFP4_HIP(launch_amax(x, dtype, M, K, K, recipe->rht_signs, ws_word(workspace, kSlotXRaw),
-                        x_rht ? ws_word(workspace, kSlotXRht) : nullptr, s));
-  NVFP4_HIP(launch_quant_tile(dtype, fx, ax, s));
+  if (fx) {
+    NVFP4_HIP(launch_amax(x, dtype, M, K, K, recipe->rht_signs, ws_word(workspace, kSlotXRaw),
+                          x_rht ? ws_word(workspace, kSlotXRht) : nullptr, s));
+    NVFP4_HIP(launch_quant_tile(dtype, fx, ax, s));
+  }
 
-  // W: 16x16 scales, with the transposed copy for Dgrad.
-  TileArgs aw;
-  aw.x = w;
-  aw.rows = N;
-  aw.cols = K;
-  aw.ld = K;
-  aw.status = ws_word(workspace, kSlotStatus);
-  aw.row = copy_args(&ctx->wq, workspace, kSlotW, nullptr);
-  aw.col = copy_args(&ctx->wqt, workspace, kSlotW, nullptr);
-  NVFP4_HIP(launch_amax(w, dtype, N, K, K, 0, ws_word(workspace, kSlotW), nullptr, s));
-  NVFP4_HIP(launch_quant_tile(dtype, kFRow | kFCol | (recipe->no_2d_weights ? 0 : kF2D), aw, s));
+  // W: 16x16 scales, with the transposed copy for Dgrad.  The BF16 forward
+  // keeps only W^T (1x16 along N on its own with no_2d_weights).
+  if (want_wt) {
+    TileArgs aw;
+    aw.x = w;
+    aw.rows = N;
+    aw.cols = K;
+    aw.ld = K;
+    aw.status = ws_word(workspace, kSlotStatus);
+    if (!bf16_fprop) aw.row = copy_args(&ctx->wq, workspace, kSlotW, nullptr);
+    aw.col = copy_args(&ctx->wqt, workspace, kSlotW, nullptr);
+    int fw = (bf16_fprop ? 0 : kFRow) | kFCol | (recipe->no_2d_weights ? 0 : kF2D);
+    NVFP4_HIP(launch_amax(w, dtype, N, K, K, 0, ws_word(workspace, kSlotW), nullptr, s));
+    NVFP4_HIP(launch_quant_tile(dtype, fw, aw, s));
+  }
 
-  // Fprop: Y = Q(X) Q(W)^T
-  NVFP4_HIP(launch_gemm(gemm_operand(&ctx->xq), gemm_operand(&ctx->wq), K, y, kDtypeBF16, N, s));
+  if (bf16_fprop) {
+    // Fprop in BF16: Y = X W^T [Review s9 precision switch; Captions Fig. 7]
+    NVFP4_HIP(launch_bf16_gemm(x, M, w, N, K, y, kDtypeBF16, N, s));
+  } else {
+    // Fprop: Y = Q(X) Q(W)^T
+    NVFP4_HIP(launch_gemm(gemm_operand(&ctx->xq), gemm_operand(&ctx->wq), K, y, kDtypeBF16, N, s));
+  }
   return NVFP4_OK;
 }
 

@@ -668,7 +668,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_lds_kernel(GemmProblem p0, Ge
     store_tile<OUT1_BF16>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
 }
 
-// ------------------------------------------------------------ MXFP4 kernel
+// ------------------------------------------------------------ MXFP4 / BF16 kernel
 //
 // The comparator format [Review "Core idea"; method summary s2]: 32-element
 // blocks of E2M1 codes with one E8M0 (power-of-two) scale each, no tensor
@@ -685,6 +685,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_lds_kernel(GemmProblem p0, Ge
 // where dword i of (half H, rl) holds the slab's four E8M0 bytes (one per
 // 32-k block) of row 128 H + 32 i + rl: one 16-byte read gives a lane its
 // four row blocks' scales for the whole slab.
+//
+// The same kernel with FMT = kFmtBf16 is the plain BF16 GEMM of the
+// precision-switch path [Review "Core idea" item (1) and the end-of-training
+// switch; Captions Fig. 7]: a slab is then 32 k of bf16 (again 64 bytes per
+// row, so the code LDS map, swizzle and loads are unchanged), a lane's 16
+// bytes are the 8 bf16 of one v_mfma_f32_32x32x16_bf16 operand, and there are
+// no scales.
+constexpr int kFmtMx = 0, kFmtBf16 = 1;
 constexpr int kMxLdsAScales = 131072, kMxLdsBScales = 135168, kMxScaleSlab = 1024;
 constexpr int kMxLdsBytes = 139264;
 constexpr int kMxSlabLoads = 10;  // per wave and slab: 4 + 4 code loads, 1 + 1 scale loads
@@ -700,9 +708,9 @@ struct MxLoader {
 // Load n (0..9) of the wave's share of slab `slab` into LDS buffer u: 0..7
 // codes (A and B alternating, 16-row groups 4w .. 4w+3), 8 A scales, 9 B
 // scales (scale load w: tile half w / 2, rows rl = 16 (w % 2) + i / 4, row
-// block i % 4 for lane i).
+// block i % 4 for lane i).  A slab is 64 bytes of every row in both formats.
 __device__ __forceinline__ void mx_load(const MxLoader& L, int slab, int u, int n) {
-  const uint32_t kc = (uint32_t)slab * (kSlabK / 2), ks = (uint32_t)slab * (kSlabK / 32);
+  const uint32_t kc = (uint32_t)slab * 64u, ks = (uint32_t)slab * (kSlabK / 32);
   if (n < 8) {
     const int q = n >> 1;
     const uint32_t q16 = (uint32_t)(4 * L.wave + q);
@@ -721,8 +729,10 @@ __device__ __forceinline__ void mx_load(const MxLoader& L, int slab, int u, int 
 
 struct MxDma {
   const MxLoader& L;
-  int slab, u;
-  __device__ __forceinline__ void operator()(int G) { mx_load(L, slab, u, G); }
+  int slab, u, nloads;  // 10 (MXFP4) or 8 (BF16: no scale loads)
+  __device__ __forceinline__ void operator()(int G) {
+    if (G < nloads) mx_load(L, slab, u, G);
+  }
 };
 
 struct MxRaw {
@@ -755,30 +765,41 @@ __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// One K-step (64 k): 16 scaled FP4 MFMAs on `cur` with the slab's scale
-// groups (byte 2 J + h of each row block's dword), in issue order; chunk G
-// also runs mem(G) and mem2(G).
-template <int J, class Mem, class Mem2>
+// One K-step: 16 MFMAs on `cur`, in issue order; chunk G also runs mem(G)
+// and mem2(G).  MXFP4: 64 k per scaled FP4 MFMA with the slab's scale
+// groups (byte 2 J + h of each row block's dword).  BF16: 16 k per MFMA.
+template <int FMT, int J, class Mem, class Mem2>
 __device__ __forceinline__ void mx_kstep(float16_t (&acc)[4][4], const MxRaw& cur, const uint4& sa,
                                          const uint4& sb, int h, Mem& mem, Mem2& mem2) {
   typedef int v8i __attribute__((ext_vector_type(8)));
+  typedef short bf16x8_t __attribute__((ext_vector_type(8)));
   const uint32_t sh = (uint32_t)(8 * (2 * J + h));
 #pragma unroll
   for (int G = 0; G < 16; ++G) {
     const int i = G >> 2, j = G & 3;
     const uint4 a = cur.ca[i], b = cur.cb[j];
-    const v8i A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-    const v8i B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-        A, B, acc[i][j], 4, 4, 0, (int)(u4_get(sa, i) >> sh), 0, (int)(u4_get(sb, j) >> sh));
+    if (FMT == kFmtMx) {
+      const v8i A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+      const v8i B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          A, B, acc[i][j], 4, 4, 0, (int)(u4_get(sa, i) >> sh), 0, (int)(u4_get(sb, j) >> sh));
+    } else {
+      bf16x8_t A, B;
+      __builtin_memcpy(&A, &a, 16);
+      __builtin_memcpy(&B, &b, 16);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[i][j], 0, 0, 0);
+    }
     mem(G);
     mem2(G);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, int FMT>
 __global__ __launch_bounds__(kGemmThreads, 1) void mxfp4_gemm_kernel(GemmProblem P) {
+  constexpr bool MX = FMT == kFmtMx;
+  constexpr int kSlabElems = MX ? kSlabK : 32;   // k per slab (64 bytes per row)
+  constexpr int kLoads = MX ? kMxSlabLoads : 8;   // BF16: code loads only
   __shared__ __align__(16) uint8_t lds[kMxLdsBytes];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -788,14 +809,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxfp4_gemm_kernel(GemmProblem
   group_tile(local, P.tiles_m, P.tiles_n, &tm, &tn);
   const GemmOperand a = P.a, b = P.b;
   const int64_t K = P.K, m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
-  const int ns = (int)(K / kSlabK);
-  const uint32_t row_bytes = (uint32_t)(K / 2), srow_bytes = (uint32_t)(K / 32);
+  const int ns = (int)(K / kSlabElems);
+  const uint32_t row_bytes = (uint32_t)(MX ? K / 2 : K * 2), srow_bytes = (uint32_t)(K / 32);
 
   MxLoader L;
   L.ca = make_rsrc(a.codes, (uint32_t)(a.rows * row_bytes));
   L.cb = make_rsrc(b.codes, (uint32_t)(b.rows * row_bytes));
-  L.sa = make_rsrc(a.scales, (uint32_t)(a.rows * srow_bytes));
-  L.sb = make_rsrc(b.scales, (uint32_t)(b.rows * srow_bytes));
+  L.sa = make_rsrc(MX ? a.scales : a.codes, MX ? (uint32_t)(a.rows * srow_bytes) : 0u);
+  L.sb = make_rsrc(MX ? b.scales : b.codes, MX ? (uint32_t)(b.rows * srow_bytes) : 0u);
   L.vca = (uint32_t)(lane >> 2) * row_bytes + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
   L.code_row_step = 16u * row_bytes;
   L.soa = (uint32_t)(m0 + 64 * wave) * row_bytes;
@@ -822,18 +843,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxfp4_gemm_kernel(GemmProblem
   float16_t acc[4][4];
   zero_acc(acc);
 #pragma unroll
-  for (int n = 0; n < kMxSlabLoads; ++n) mx_load(L, 0, 0, n);
+  for (int n = 0; n < kLoads; ++n) mx_load(L, 0, 0, n);
 #pragma unroll
-  for (int n = 0; n < kMxSlabLoads; ++n) mx_load(L, 1, 1, n);
+  for (int n = 0; n < kLoads; ++n) mx_load(L, 1, 1, n);
 #pragma unroll
-  for (int n = 0; n < kMxSlabLoads; ++n) mx_load(L, 2, 2, n);
-  wait_vmcnt<2 * kMxSlabLoads>();
+  for (int n = 0; n < kLoads; ++n) mx_load(L, 2, 2, n);
+  wait_vmcnt<2 * kLoads>();
   __builtin_amdgcn_s_barrier();
 
   MxRaw r0, r1;
-  uint4 sa, sb, sa_n, sb_n;
+  uint4 sa = make_uint4(0, 0, 0, 0), sb = sa, sa_n = sa, sb_n = sa;
   {
-    MxMem<0, true> first{lds, rca[0], rcb[0], rsa, rsb, 0, r0, sa, sb};
+    MxMem<0, MX> first{lds, rca[0], rcb[0], rsa, rsb, 0, r0, sa, sb};
 #pragma unroll
     for (int idx = 0; idx < 10; ++idx) first(idx);
   }
@@ -841,12 +862,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxfp4_gemm_kernel(GemmProblem
     const int u = s & 3;
     MxMem<1, false> m1{lds, rca[1], rcb[1], rsa, rsb, u, r1, sa_n, sb_n};
     NoMem none;
-    mx_kstep<0>(acc, r0, sa, sb, h, m1, none);
-    wait_vmcnt<kMxSlabLoads>();
+    mx_kstep<FMT, 0>(acc, r0, sa, sb, h, m1, none);
+    wait_vmcnt<kLoads>();
     __builtin_amdgcn_s_barrier();
-    MxMem<0, true> m0{lds, rca[0], rcb[0], rsa, rsb, (u + 1) & 3, r0, sa_n, sb_n};
-    MxDma dma{L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3};
-    mx_kstep<1>(acc, r1, sa, sb, h, m0, dma);
+    MxMem<0, MX> m0{lds, rca[0], rcb[0], rsa, rsb, (u + 1) & 3, r0, sa_n, sb_n};
+    MxDma dma{L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3, kLoads};
+    mx_kstep<FMT, 1>(acc, r1, sa, sb, h, m0, dma);
     sa = sa_n;
     sb = sb_n;
   }
@@ -935,9 +956,22 @@ hipError_t launch_mx_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K,
   const GemmProblem p = make_problem(a, b, K, c, ldc);
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kGemmThreads);
   if (c_dtype == kDtypeBF16)
-    hipLaunchKernelGGL((mxfp4_gemm_kernel<true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((mxfp4_gemm_kernel<true, kFmtMx>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((mxfp4_gemm_kernel<false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((mxfp4_gemm_kernel<false, kFmtMx>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_gemm(const void* a, int64_t M, const void* b, int64_t N, int64_t K, void* c,
+                            int c_dtype, int64_t ldc, hipStream_t s) {
+  GemmOperand oa{static_cast<const uint8_t*>(a), nullptr, nullptr, M, 0};
+  GemmOperand ob{static_cast<const uint8_t*>(b), nullptr, nullptr, N, 0};
+  const GemmProblem p = make_problem(oa, ob, K, c, ldc);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kGemmThreads);
+  if (c_dtype == kDtypeBF16)
+    hipLaunchKernelGGL((mxfp4_gemm_kernel<true, kFmtBf16>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((mxfp4_gemm_kernel<false, kFmtBf16>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

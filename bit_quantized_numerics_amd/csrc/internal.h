@@ -69,6 +69,10 @@ hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, vo
 // Requires K % 128 == 0, K >= 384 and rows * K / 2 < 2^31 for both operands.
 hipError_t launch_mx_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c,
                           int c_dtype, int64_t ldc, hipStream_t s);
+// Plain BF16 GEMM C = A B^T, A [M, K] and B [N, K] dense bf16 (row stride K),
+// FP32 accumulation.  Requires K % 32 == 0, K >= 96, rows * K * 2 < 2^31.
+hipError_t launch_bf16_gemm(const void* a, int64_t M, const void* b, int64_t N, int64_t K, void* c,
+                            int c_dtype, int64_t ldc, hipStream_t s);
 // Two independent GEMMs in one launch where the kernel allows it (so that the
 // tail of one fills with the tiles of the other), else two launches.
 hipError_t launch_gemm_pair(const GemmOperand& a0, const GemmOperand& b0, int64_t K0, void* c0,

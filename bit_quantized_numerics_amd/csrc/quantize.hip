@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
   bool do_row = false, do_col = false;
   if (ROW) do_row = copy_scales(a.row.amax, a.status, &tr);
   if (COL) {
-    if (TWO_D) {
+    if (TWO_D && ROW) {
       do_col = do_row;
       tc = tr;
     } else {
@@ -244,18 +244,22 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
       for (int j = 0; j < 8; ++j) am = fmaxf(am, __builtin_fabsf(v[i][j]));
     am = fmaxf(am, lane_xor1(am));
     uint32_t dcode;
-    const float r = block_scale(am, tr, &dcode);
+    // without the row copy (W^T only) the tensor scales come from the column slot
+    const float r = block_scale(am, ROW ? tr : tc, &dcode);
     if (valid) {
       const int64_t gcols = cols / 16, grows = rows / 16;
+      if (ROW) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s[8];
+        for (int i = 0; i < 16; ++i) {
+          float s[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s[j] = v[i][j] * r;
-        *reinterpret_cast<uint32_t*>(a.row.codes + (r0 + i) * (cols / 2) + c0 / 2) = fp4x8_rn(s);
+          for (int j = 0; j < 8; ++j) s[j] = v[i][j] * r;
+          *reinterpret_cast<uint32_t*>(a.row.codes + (r0 + i) * (cols / 2) + c0 / 2) =
+              fp4x8_rn(s);
+        }
       }
       if ((cg & 1) == 0) {
-        a.row.scales[(r0 / 16) * gcols + c0 / 16] = (uint8_t)dcode;
+        if (ROW) a.row.scales[(r0 / 16) * gcols + c0 / 16] = (uint8_t)dcode;
         if (COL) a.col.scales[(c0 / 16) * grows + r0 / 16] = (uint8_t)dcode;
       }
       if (COL) {
@@ -359,6 +363,7 @@ static bool tile_dispatch(int flags, const TileArgs& a, hipStream_t s) {
     NVFP4_CASE(kFRow | kFCol | kFRht | kFSrCol)
     NVFP4_CASE(kFRow | kF2D)
     NVFP4_CASE(kFRow | kFCol | kF2D)
+    NVFP4_CASE(kFCol | kF2D)
 #undef NVFP4_CASE
     default:
       return false;

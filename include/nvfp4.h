@@ -112,18 +112,22 @@ typedef struct {
   uint32_t stream_id;
 } nvfp4_quant_opts;
 
-/* The pages' layer recipe [Review "Core idea" items (2)-(4); Captions
- * Fig. 5]: 16x16 weight scales, RHT on the Wgrad inputs only, stochastic
- * rounding on the gradient copies only.  The pages fix one sign seed for the
- * whole run: use nvfp4_rht_signs_from_seed(0) unless another is wanted. */
 /* The layer recipe.  All-zero switches give the pages' recipe [Review "Core
- * idea" items (2)-(4); Captions Fig. 4]; each switch removes one component,
- * as the pages' ablations do [Captions Fig. 4, 10, 11, 14]:
+ * idea" items (2)-(4); Captions Fig. 4, 5]: 16x16 weight scales, RHT on the
+ * Wgrad inputs only, stochastic rounding on the gradient copies only.  The
+ * pages fix one sign seed for the whole run: use nvfp4_rht_signs_from_seed(0)
+ * unless another is wanted.  Each no_* switch removes one component, as the
+ * pages' ablations do [Captions Fig. 4, 10, 11, 14]:
  *   no_2d_weights  W and W^T are each quantised with 1x16 blocks along their
  *                  own rows (W along K for Fprop, W^T along N for Dgrad), so
  *                  the two copies differ (w_fprop != w_bprop) [Review s2]
  *   no_rht         the Wgrad copies (X^T, dY^T) skip the RHT
  *   no_sr          the dY copies round to nearest-even
+ *   bf16_fprop     the end-of-training precision switch [Review s9; Captions
+ *                  Fig. 7]: Fprop runs as the plain BF16 product Y = X W^T
+ *                  (nvfp4_bf16_gemm) while the backward stays NVFP4.  Needs
+ *                  dtype NVFP4_BF16 and K % 32 == 0, K >= 96; ctx->xq and
+ *                  ctx->wq are then neither read nor written.
  * A backward must use the recipe of its forward. */
 typedef struct {
   uint32_t rht_signs;   /* sign diagonal shared by every RHT of the layer */
@@ -131,6 +135,7 @@ typedef struct {
   int32_t no_2d_weights;
   int32_t no_rht;
   int32_t no_sr;
+  int32_t bf16_fprop;
 } nvfp4_recipe;
 
 /* Buffers of one layer step Y = X W^T, X [M, K], W [N, K], dY [M, N].
@@ -288,11 +293,26 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, i
                         int64_t ldc, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * nvfp4_bf16_gemm: the plain BF16 product C = A B^T with FP32 accumulation,
+ * the high-precision forward of the pages' precision switch [Review s9;
+ * Captions Fig. 7].  a: bf16 [M, K], b: bf16 [N, K], both dense row-major
+ * (row stride K) and 16-byte aligned; c: [M, N] row-major with leading dim
+ * ldc >= N, c_dtype NVFP4_F32 or NVFP4_BF16 (rounded to nearest-even), aligned
+ * to its element.  M, N >= 1 (any value); K % 32 == 0 and K >= 96; each
+ * operand's rows rounded up to 256, times K * 2 bytes, below 2^31
+ * (else NVFP4_ERR_SHAPE).  Needs no workspace.
+ */
+nvfp4_status nvfp4_bf16_gemm(const void* a, const void* b, void* c, int64_t M, int64_t N,
+                             int64_t K, int32_t c_dtype, int64_t ldc, void* stream);
+
+/*
  * nvfp4_linear_fwd: forward of one NVFP4 linear layer Y = X W^T [Review s6
  * step 1; Captions Fig. 5].  Quantises X (1x16 RN -> ctx->xq), W (16x16 RN ->
  * ctx->wq and ctx->wqt) and, when recipe->training, (R X)^T (RHT along
  * tokens, RN -> ctx->xqt), then runs the Fprop GEMM.  x [M, K], w [N, K] of
- * `dtype`, dense; y [M, N] bf16.  M, K, N multiples of 16.
+ * `dtype`, dense; y [M, N] bf16.  M, K, N multiples of 16.  With
+ * recipe->bf16_fprop only the backward copies (ctx->wqt, and ctx->xqt when
+ * training) are made and Fprop is nvfp4_bf16_gemm(x, w).
  */
 nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, int64_t K,
                               int64_t N, int32_t dtype, const nvfp4_recipe* recipe,

@@ -309,6 +309,9 @@ class Recipe:
     weights_2d: bool = True
     rht: bool = True
     sr: bool = True
+    # the end-of-training precision switch [Review s9; Captions Fig. 7]:
+    # Fprop is the plain BF16 product bf16_gemm(x, w); the backward is unchanged
+    bf16_fprop: bool = False
 
 
 def linear_operands(x, w, dy, recipe: Recipe):
@@ -320,14 +323,19 @@ def linear_operands(x, w, dy, recipe: Recipe):
       dyq  dY, 1x16 along N, stochastic, stream 0    (Dgrad A)
       dyqt (R dY)^T, RHT along tokens, stochastic, stream 1  (Wgrad A)
       xqt  (R X)^T,  RHT along tokens, nearest-even  (Wgrad B)
-    dy may be None (forward only)."""
+    dy may be None (forward only).  With recipe.bf16_fprop the Fprop operands
+    xq and wq are not made."""
     s = recipe.rht_signs
     ops = {}
-    ops["xq"] = quantize(x)
+    if not recipe.bf16_fprop:
+        ops["xq"] = quantize(x)
     if recipe.weights_2d:
-        ops["wq"], ops["wqt"] = quantize_2d(w)
+        wq, ops["wqt"] = quantize_2d(w)
+        if not recipe.bf16_fprop:
+            ops["wq"] = wq
     else:
-        ops["wq"] = quantize(w)
+        if not recipe.bf16_fprop:
+            ops["wq"] = quantize(w)
         ops["wqt"] = quantize(w, transpose=True)
     ops["xqt"] = quantize(x, transpose=True, rht=recipe.rht, signs=s)
     if dy is not None:
@@ -342,7 +350,7 @@ __all__ = [
     "gemm_entries", "dequant_rows", "rht16", "philox4x32_10", "sr_bits", "sr_bits_n",
     "rht_signs_from_seed", "e2m1_decode", "e4m3_decode", "e4m3_encode",
     "e2m1_rn_index", "e2m1_sr_index", "e4m3_encode_n", "e2m1_rn_index_n",
-    "e2m1_sr_index_n", "linear_operands", "lib",
+    "e2m1_sr_index_n", "linear_operands", "lib", "bf16_values", "bf16_gemm",
 ]
 
 
@@ -421,3 +429,28 @@ def rht(x, axis: int, d: int, signs) -> np.ndarray:
     if st:
         raise OracleError(st)
     return y
+
+
+# ---------------------------------------------------------------- BF16 Fprop
+# The high-precision forward of the precision switch [Review s9; Captions
+# Fig. 7]: Y = X W^T on the bf16 values themselves, no quantisation.
+
+
+def bf16_values(x) -> np.ndarray:
+    """float64 values of bf16 data given as float32 (or float64) numbers;
+    raises ValueError for a value bf16 cannot hold (low 16 bits of its fp32
+    pattern not zero), so a caller cannot pass unrounded data by mistake."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if np.any(f.view(np.uint32) & 0xFFFF):
+        raise ValueError("bf16_values: input not representable in bfloat16")
+    return f.astype(np.float64)
+
+
+def bf16_gemm(a, b):
+    """C = A B^T and S = |A| |B|^T in float64 for bf16 A [M, K], B [N, K]
+    (the float64 matmul is a library primitive; every product of two bf16
+    values is exact in float64)."""
+    ah, bh = bf16_values(a), bf16_values(b)
+    if ah.ndim != 2 or bh.ndim != 2 or ah.shape[1] != bh.shape[1]:
+        raise OracleError(ERR_SHAPE)
+    return ah @ bh.T, np.abs(ah) @ np.abs(bh).T

@@ -163,3 +163,25 @@ def test_2d_rht_and_layer_argument_errors():
     # backward before a training forward on this ctx
     assert nv._lib.nvfp4_linear_bwd(P, nv.BF16, ctypes.byref(ctx), P, P, nv.F32, 1,
                                     ctypes.byref(rec), P, WSB, None) == nv.ERR_SHAPE
+
+
+def test_bf16_gemm_and_switch_argument_errors():
+    f = nv._lib.nvfp4_bf16_gemm
+    assert f(None, P, P, 64, 128, 256, nv.F32, 128, None) == nv.ERR_NULL
+    assert f(P, P, None, 64, 128, 256, nv.F32, 128, None) == nv.ERR_NULL
+    assert f(P, P, P, 64, 128, 256, 7, 128, None) == nv.ERR_DTYPE
+    assert f(P, P, P, 64, 128, 64, nv.F32, 128, None) == nv.ERR_SHAPE     # K < 96
+    assert f(P, P, P, 64, 128, 272, nv.F32, 128, None) == nv.ERR_SHAPE    # K % 32
+    assert f(P, P, P, 0, 128, 256, nv.F32, 128, None) == nv.ERR_SHAPE     # M
+    assert f(P, P, P, 64, 128, 256, nv.F32, 100, None) == nv.ERR_SHAPE    # ldc < N
+    assert f(P, P, P, 1 << 22, 128, 256, nv.F32, 128, None) == nv.ERR_SHAPE  # 32-bit offsets
+    assert f(P + 8, P, P, 64, 128, 256, nv.F32, 128, None) == nv.ERR_ALIGN
+    assert f(P, P, P + 2, 64, 128, 256, nv.F32, 128, None) == nv.ERR_ALIGN
+    t = _tensor()
+    ctx = nv.c_linear_ctx(0, 0, 0, t, t, t, t, t, t)
+    rec = nv.c_recipe(0, 1, 0, 0, 0, 1)
+    # the BF16 forward needs bf16 inputs and K % 32 == 0
+    assert nv._lib.nvfp4_linear_fwd(P, P, P, 64, 256, 64, nv.F32, ctypes.byref(rec),
+                                    ctypes.byref(ctx), P, WSB, None) == nv.ERR_DTYPE
+    assert nv._lib.nvfp4_linear_fwd(P, P, P, 64, 272, 64, nv.BF16, ctypes.byref(rec),
+                                    ctypes.byref(ctx), P, WSB, None) == nv.ERR_SHAPE
