@@ -84,8 +84,6 @@ def copy_reference(mib: int) -> None:
 def cpu_baseline(sample_tokens: int):
     """The oracle, as it stands, on a bounded sample of the same step: the
     layer with `sample_tokens` tokens (W stays full size)."""
-    import numpy as np
-
     import oracle as O
     import workloads as W
     Ms = sample_tokens
@@ -102,7 +100,6 @@ def cpu_baseline(sample_tokens: int):
     t2 = time.perf_counter()
     flops = 3 * 2.0 * Ms * N * K
     qbytes = BYTES_ROWCOL * (Ms * K + Ms * N) + BYTES_2D * N * K
-    _ = np
     return {
         "value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"one layer step at {Ms} tokens (K={K}, N={N}, W full size): all six "
@@ -198,8 +195,8 @@ def mxfp4_comparator(nv, x, w, reps: int):
 
 
 def bf16_fprop(nv, x, w, ctx, ws, signs, reps: int):
-    """The precision switch's forward [Review s9; Captions Fig. 7] on the
-    Fprop shape: the plain BF16 GEMM alone, and the training forward with
+    """The precision switch's forward [Review "Core strengths" item 9;
+    Captions Fig. 7] on the Fprop shape: the plain BF16 GEMM alone, and the training forward with
     bf16_fprop (backward copies of X and W, then the BF16 GEMM) next to the
     NVFP4 training forward, timed with HIP events on the launch stream."""
     import torch

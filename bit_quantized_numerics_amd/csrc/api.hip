@@ -516,7 +516,7 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
   }
 
   if (bf16_fprop) {
-    // Fprop in BF16: Y = X W^T [Review s9 precision switch; Captions Fig. 7]
+    // Fprop in BF16: Y = X W^T [Review "Core strengths" item 9; Captions Fig. 7]
     NVFP4_HIP(launch_bf16_gemm(x, M, w, N, K, y, kDtypeBF16, N, s));
   } else {
     // Fprop: Y = Q(X) Q(W)^T

@@ -670,8 +670,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_lds_kernel(GemmProblem p0, Ge
 
 // ------------------------------------------------------------ MXFP4 / BF16 kernel
 //
-// The comparator format [Review "Core idea"; method summary s2]: 32-element
-// blocks of E2M1 codes with one E8M0 (power-of-two) scale each, no tensor
+// The comparator format [Review "secret weapon" items 1-2; Captions Fig. 6]:
+// 32-element blocks of E2M1 codes with one E8M0 (power-of-two) scale each, no tensor
 // scale.  gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 computes exactly this
 // product: lane l supplies row l % 32's codes k = 32 (l / 32) .. +31 (16
 // bytes, low nibble = even k) and byte 0 of a scale VGPR for that 32-element
@@ -687,8 +687,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_lds_kernel(GemmProblem p0, Ge
 // four row blocks' scales for the whole slab.
 //
 // The same kernel with FMT = kFmtBf16 is the plain BF16 GEMM of the
-// precision-switch path [Review "Core idea" item (1) and the end-of-training
-// switch; Captions Fig. 7]: a slab is then 32 k of bf16 (again 64 bytes per
+// end-of-training precision switch [Review "Core strengths" item 9; Captions
+// Fig. 7]: a slab is then 32 k of bf16 (again 64 bytes per
 // row, so the code LDS map, swizzle and loads are unchanged), a lane's 16
 // bytes are the 8 bf16 of one v_mfma_f32_32x32x16_bf16 operand, and there are
 // no scales.

@@ -568,8 +568,8 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const flo
 
 // ---------------------------------------------------------------- MXFP4
 
-// MXFP4 comparator [Review "Core idea"; method summary s2]: one thread per
-// 32-element block along cols.  Scale e = floor(log2(amax)) - 2 clamped to
+// MXFP4 comparator [Review "secret weapon" items 1-2; Captions Fig. 6]: one
+// thread per 32-element block along cols.  Scale e = floor(log2(amax)) - 2 clamped to
 // [-127, 127] (E8M0 code e + 127; an all-zero block stores code 0, a block
 // holding Inf/NaN the NaN code 0xFF with zero codes); elements
 // x * 2^-e (exact) to E2M1 nearest-even, saturating at 6.

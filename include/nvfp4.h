@@ -66,8 +66,8 @@ typedef enum {
 typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
 typedef enum { NVFP4_RN = 0, NVFP4_SR = 1 } nvfp4_round;
 /* NVFP4_SCALE_MX32 marks an MXFP4 operand, the comparator format the pages
- * weigh NVFP4 against [Review "Core idea"; method summary s2]: the same
- * codes, one E8M0 (power-of-two, bias 127) scale per 32 elements of a row,
+ * weigh NVFP4 against [Review "secret weapon" items 1-2; Captions Fig. 6]:
+ * the same codes, one E8M0 (power-of-two, bias 127) scale per 32 elements of a row,
  * scales [rows][cols/32], no tensor scale (global_scale unused, may be NULL). */
 typedef enum {
   NVFP4_SCALE_1X16 = 0,
@@ -123,8 +123,9 @@ typedef struct {
  *                  the two copies differ (w_fprop != w_bprop) [Review s2]
  *   no_rht         the Wgrad copies (X^T, dY^T) skip the RHT
  *   no_sr          the dY copies round to nearest-even
- *   bf16_fprop     the end-of-training precision switch [Review s9; Captions
- *                  Fig. 7]: Fprop runs as the plain BF16 product Y = X W^T
+ *   bf16_fprop     the end-of-training precision switch [Review "Core
+ *                  strengths" item 9; Captions Fig. 7]: Fprop runs as the
+ *                  plain BF16 product Y = X W^T
  *                  (nvfp4_bf16_gemm) while the backward stays NVFP4.  Needs
  *                  dtype NVFP4_BF16 and K % 32 == 0, K >= 96; ctx->xq and
  *                  ctx->wq are then neither read nor written.
@@ -252,8 +253,8 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor* t, float* out, int64_t ldo, vo
 /*
  * nvfp4_mx_quantize: MXFP4 quantisation of x [rows, cols] (leading dim ld,
  * F32 or BF16) with 32-element blocks along cols (cols % 32 == 0), the
- * comparator of [Review "Core idea"; method summary s2: blocks of 32, one
- * power-of-two UE8M0 scale].  Scale rule (the OCP Microscaling one; the
+ * comparator of [Review "secret weapon" items 1-2; Captions Fig. 6]: blocks
+ * of 32, one power-of-two UE8M0 scale.  Scale rule (the OCP Microscaling one; the
  * pages describe only the format): e = floor(log2(amax_b)) - 2 clamped to
  * [-127, 127], stored as e + 127; so amax_b / 2^e is in [4, 8) and values at
  * or above 6 * 2^e saturate (the binade the pages say MXFP4 loses).  An
@@ -294,8 +295,8 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, i
 
 /*
  * nvfp4_bf16_gemm: the plain BF16 product C = A B^T with FP32 accumulation,
- * the high-precision forward of the pages' precision switch [Review s9;
- * Captions Fig. 7].  a: bf16 [M, K], b: bf16 [N, K], both dense row-major
+ * the high-precision forward of the pages' precision switch [Review "Core
+ * strengths" item 9; Captions Fig. 7].  a: bf16 [M, K], b: bf16 [N, K], both dense row-major
  * (row stride K) and 16-byte aligned; c: [M, N] row-major with leading dim
  * ldc >= N, c_dtype NVFP4_F32 or NVFP4_BF16 (rounded to nearest-even), aligned
  * to its element.  M, N >= 1 (any value); K % 32 == 0 and K >= 96; each

@@ -309,8 +309,9 @@ class Recipe:
     weights_2d: bool = True
     rht: bool = True
     sr: bool = True
-    # the end-of-training precision switch [Review s9; Captions Fig. 7]:
-    # Fprop is the plain BF16 product bf16_gemm(x, w); the backward is unchanged
+    # the end-of-training precision switch [Review "Core strengths" item 9;
+    # Captions Fig. 7]: Fprop is the plain BF16 product bf16_gemm(x, w); the
+    # backward is unchanged
     bf16_fprop: bool = False
 
 
@@ -355,8 +356,8 @@ __all__ = [
 
 
 # ---------------------------------------------------------------- MXFP4
-# The comparator format [Review "Core idea"; method summary s2]: 32-element
-# blocks, one power-of-two (UE8M0) scale each, no tensor scale.  Scale rule
+# The comparator format [Review "secret weapon" items 1-2; Captions Fig. 6]:
+# 32-element blocks, one power-of-two (UE8M0) scale each, no tensor scale.  Scale rule
 # (a reading; the pages only describe the format): e = floor(log2(amax_b)) - 2.
 
 
@@ -432,8 +433,8 @@ def rht(x, axis: int, d: int, signs) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- BF16 Fprop
-# The high-precision forward of the precision switch [Review s9; Captions
-# Fig. 7]: Y = X W^T on the bf16 values themselves, no quantisation.
+# The high-precision forward of the precision switch [Review "Core strengths"
+# item 9; Captions Fig. 7]: Y = X W^T on the bf16 values themselves, no quantisation.
 
 
 def bf16_values(x) -> np.ndarray:

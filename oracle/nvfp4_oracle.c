@@ -495,9 +495,10 @@ void oracle_sr_bits_n(uint64_t seed, uint32_t stream, uint64_t e0, int64_t n, ui
 }
 
 /* ------------------------------------------------------------------------ */
-/* MXFP4, the comparator format the pages weigh NVFP4 against [Review "Core  */
-/* idea" and s2 of the method summary: blocks of 32 E2M1 values sharing one  */
-/* power-of-two UE8M0 scale, no tensor scale; the pages attribute its loss  */
+/* MXFP4, the comparator format the pages weigh NVFP4 against [Review      */
+/* "secret weapon" items 1-2; Captions Fig. 6: blocks of 32 E2M1 values     */
+/* sharing one power-of-two UE8M0 scale, no tensor scale; the pages         */
+/* attribute its loss                                                       */
 /* to that power-of-two rounding dropping a binade (values near +-4, +-6)].  */
 /* The pages do not spell the scale rule out; the reading taken is the OCP  */
 /* Microscaling rule: X = 2^e with e = floor(log2(amax_b)) - 2 (2 is E2M1's */

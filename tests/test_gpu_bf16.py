@@ -1,5 +1,5 @@
-"""GPU parity of the BF16 forward of the precision switch [Review s9;
-Captions Fig. 7]: nvfp4_bf16_gemm against the oracle's float64 product of
+"""GPU parity of the BF16 forward of the precision switch [Review "Core
+strengths" item 9; Captions Fig. 7]: nvfp4_bf16_gemm against the oracle's float64 product of
 the same bf16 values, and nvfp4_linear_fwd with bf16_fprop (Y from the BF16
 product, the backward copies bit-exact against the oracle and the backward
 unchanged bit for bit)."""

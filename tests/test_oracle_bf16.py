@@ -1,5 +1,5 @@
 """Pins of the oracle's BF16 forward, the high-precision Fprop of the
-precision switch [Review s9; Captions Fig. 7].
+precision switch [Review "Core strengths" item 9; Captions Fig. 7].
 
 The oracle computes C = A B^T on the bf16 values in float64.  The pins fix
 it against things other than itself: exact rational sums on tiny inputs, a

@@ -1,7 +1,7 @@
 """Pins of the oracle's MXFP4 comparator (CPU only).
 
-MXFP4 as the pages describe it [Review "Core idea"; method summary s2]: blocks
-of 32 E2M1 values with one power-of-two (UE8M0) scale, no tensor scale; the
+MXFP4 as the pages describe it [Review "secret weapon" items 1-2; Captions
+Fig. 6]: blocks of 32 E2M1 values with one power-of-two (UE8M0) scale, no tensor scale; the
 pages attribute MXFP4's extra loss to that power-of-two rounding losing a
 binade around +-4 / +-6.  The scale rule is the OCP Microscaling one,
 e = floor(log2(amax)) - 2 (a reading; the pages do not spell it out), and the
