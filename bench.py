@@ -44,8 +44,8 @@ BYTES_2D = 2.0 + 2 * (0.5 + 1.0 / 256)
 # 1 GiB device copy reads back), averaged over the single Fprop, Dgrad and
 # Wgrad launches: 1072.7, 875.8 and 1286.5 MB.  Valid only for the kernel
 # source it was measured on (profiles/hbm_traffic_gemm_quantize_*.md).
-GEMM_TRAFFIC = {"source_sha1": "4570dc821782b18f402e5dd83fcab18bd77b88af",
-                "bytes_per_launch": 1078.3e6}
+GEMM_TRAFFIC = {"source_sha1": "eadad7b74f082e746c07128b72f2ce26293f7e98",
+                "bytes_per_launch": 1078.4e6}
 
 
 def _gemm_source_sha1() -> str:
