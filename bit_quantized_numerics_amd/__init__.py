@@ -79,6 +79,8 @@ _SIGS = {
     "nvfp4_rht_signs128_from_seed": (None, [_u64, ctypes.POINTER(_u32)]),
     "nvfp4_gemm": (_i32, [_T, _T, _vp, _i32, _i64, _vp, _sz, _vp]),
     "nvfp4_bf16_gemm": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
+    "nvfp4_linear_ctx_bytes": (_i32, [_i64, _i64, _i64, ctypes.POINTER(_sz)]),
+    "nvfp4_linear_ctx_init": (_i32, [ctypes.POINTER(c_linear_ctx), _vp, _sz, _i64, _i64, _i64]),
     "nvfp4_linear_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.POINTER(c_recipe),
                                 ctypes.POINTER(c_linear_ctx), _vp, _sz, _vp]),
     "nvfp4_linear_bwd": (_i32, [_vp, _i32, ctypes.POINTER(c_linear_ctx), _vp, _vp, _i32, _u64,
@@ -331,6 +333,12 @@ def nvfp4_bf16_gemm(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.float32,
     return c
 
 
+def nvfp4_linear_ctx_bytes(M: int, K: int, N: int) -> int:
+    out = _sz(0)
+    _check(_lib.nvfp4_linear_ctx_bytes(M, K, N, ctypes.byref(out)), "nvfp4_linear_ctx_bytes")
+    return out.value
+
+
 class LinearContext:
     """Caller-owned quantised operands of one layer step (Y = X W^T)."""
 
@@ -345,6 +353,28 @@ class LinearContext:
         self.dyqt = NVFP4Tensor(N, M, device=device)
         self.cctx = c_linear_ctx(M, K, N, self.xq.c(), self.wq.c(), self.wqt.c(), self.xqt.c(),
                                  self.dyq.c(), self.dyqt.c())
+
+    @classmethod
+    def from_buffer(cls, M: int, K: int, N: int, device="cuda"):
+        """All six operands in one device buffer laid out by nvfp4_linear_ctx_init."""
+        nbytes = nvfp4_linear_ctx_bytes(M, K, N)
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self = cls.__new__(cls)
+        self.M, self.K, self.N, self.buffer = M, K, N, buf
+        self.cctx = c_linear_ctx()
+        _check(_lib.nvfp4_linear_ctx_init(ctypes.byref(self.cctx), ctypes.c_void_p(buf.data_ptr()),
+                                          nbytes, M, K, N), "nvfp4_linear_ctx_init")
+        base = buf.data_ptr()
+        for name in ("xq", "wq", "wqt", "xqt", "dyq", "dyqt"):
+            ct = getattr(self.cctx, name)
+            t = NVFP4Tensor.__new__(NVFP4Tensor)
+            t.rows, t.cols, t.scale_mode = ct.rows, ct.cols, ct.scale_mode
+            n_codes, n_scales = ct.rows * ct.cols // 2, ct.rows * ct.cols // 16
+            t.codes = buf[ct.codes - base:ct.codes - base + n_codes]
+            t.scales = buf[ct.scales - base:ct.scales - base + n_scales]
+            t.global_scale = buf[ct.global_scale - base:ct.global_scale - base + 4].view(torch.float32)
+            setattr(self, name, t)
+        return self
 
     def sync_shapes(self):
         for name in ("xq", "wq", "wqt", "xqt", "dyq", "dyqt"):

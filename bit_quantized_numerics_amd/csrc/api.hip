@@ -163,6 +163,22 @@ void set_shape(nvfp4_tensor* t, int64_t rows, int64_t cols, int32_t mode) {
 
 }  // namespace
 
+namespace {
+
+// The six operands of a layer step in ctx order, with their shapes: xq [M, K],
+// wq [N, K], wqt [K, N], xqt [K, M], dyq [M, N], dyqt [N, M].  Scale arrays
+// are sized for 1x16 blocks so that either weight recipe fits.
+void ctx_shapes(int64_t M, int64_t K, int64_t N, int64_t (&rc)[6][2]) {
+  const int64_t s[6][2] = {{M, K}, {N, K}, {K, N}, {K, M}, {M, N}, {N, M}};
+  for (int i = 0; i < 6; ++i) {
+    rc[i][0] = s[i][0];
+    rc[i][1] = s[i][1];
+  }
+}
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
 extern "C" {
 
 nvfp4_status nvfp4_tensor_bytes(int64_t rows, int64_t cols, int32_t scale_mode, size_t* codes_bytes,
@@ -185,6 +201,49 @@ nvfp4_status nvfp4_tensor_bytes(int64_t rows, int64_t cols, int32_t scale_mode, 
 }
 
 size_t nvfp4_workspace_bytes(void) { return kWorkspaceBytes; }
+
+nvfp4_status nvfp4_linear_ctx_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes) {
+  if (!bytes) return NVFP4_ERR_NULL;
+  if (M <= 0 || K <= 0 || N <= 0 || M % 16 || K % 16 || N % 16) return NVFP4_ERR_SHAPE;
+  int64_t rc[6][2];
+  ctx_shapes(M, K, N, rc);
+  size_t total = 0;
+  for (int i = 0; i < 6; ++i) {
+    total += align256((size_t)(rc[i][0] * (rc[i][1] / 2)));   // codes
+    total += align256((size_t)(rc[i][0] * (rc[i][1] / 16)));  // 1x16-sized scales
+    total += 256;                                              // tensor scale
+  }
+  *bytes = total;
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_linear_ctx_init(nvfp4_linear_ctx* ctx, void* buffer, size_t bytes, int64_t M,
+                                   int64_t K, int64_t N) {
+  if (!ctx || !buffer) return NVFP4_ERR_NULL;
+  size_t need = 0;
+  NVFP4_TRY(nvfp4_linear_ctx_bytes(M, K, N, &need));
+  if (bytes < need) return NVFP4_ERR_SHAPE;
+  if (!aligned(buffer, 256)) return NVFP4_ERR_ALIGN;
+  int64_t rc[6][2];
+  ctx_shapes(M, K, N, rc);
+  nvfp4_tensor* t[6] = {&ctx->xq, &ctx->wq, &ctx->wqt, &ctx->xqt, &ctx->dyq, &ctx->dyqt};
+  const int32_t modes[6] = {NVFP4_SCALE_1X16, NVFP4_SCALE_16X16, NVFP4_SCALE_16X16,
+                            NVFP4_SCALE_1X16, NVFP4_SCALE_1X16,  NVFP4_SCALE_1X16};
+  uint8_t* p = static_cast<uint8_t*>(buffer);
+  for (int i = 0; i < 6; ++i) {
+    t[i]->codes = p;
+    p += align256((size_t)(rc[i][0] * (rc[i][1] / 2)));
+    t[i]->scales = p;
+    p += align256((size_t)(rc[i][0] * (rc[i][1] / 16)));
+    t[i]->global_scale = reinterpret_cast<float*>(p);
+    p += 256;
+    set_shape(t[i], rc[i][0], rc[i][1], modes[i]);
+  }
+  ctx->M = M;
+  ctx->K = K;
+  ctx->N = N;
+  return NVFP4_OK;
+}
 
 uint32_t nvfp4_rht_signs_from_seed(uint64_t seed) {
   uint32_t c[4] = {0u, 0u, 0u, 0u};

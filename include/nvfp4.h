@@ -160,6 +160,21 @@ typedef struct {
 nvfp4_status nvfp4_tensor_bytes(int64_t rows, int64_t cols, int32_t scale_mode,
                                 size_t* codes_bytes, size_t* scales_bytes);
 
+/* Bytes of one device buffer that holds all six quantised operands of a
+ * layer step (the buffers of nvfp4_linear_ctx), for nvfp4_linear_ctx_init.
+ * M, K, N positive multiples of 16. */
+nvfp4_status nvfp4_linear_ctx_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes);
+
+/* Point ctx's six operands into `buffer` (a device buffer of at least
+ * nvfp4_linear_ctx_bytes(M, K, N) bytes, 256-byte aligned; the caller keeps
+ * ownership) and set their shapes and ctx->M, K, N.  Codes, scales and tensor
+ * scale of each operand start on 256-byte boundaries; scale arrays are sized
+ * for 1x16 blocks, so either weight recipe fits.  Host bookkeeping only:
+ * nothing is enqueued and the buffer is not touched.  A buffer that is too
+ * small is NVFP4_ERR_SHAPE. */
+nvfp4_status nvfp4_linear_ctx_init(nvfp4_linear_ctx* ctx, void* buffer, size_t bytes, int64_t M,
+                                   int64_t K, int64_t N);
+
 /* Minimum workspace size in bytes (a constant, 32 KB). */
 size_t nvfp4_workspace_bytes(void);
 

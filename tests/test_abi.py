@@ -185,3 +185,33 @@ def test_bf16_gemm_and_switch_argument_errors():
                                     ctypes.byref(ctx), P, WSB, None) == nv.ERR_DTYPE
     assert nv._lib.nvfp4_linear_fwd(P, P, P, 64, 272, 64, nv.BF16, ctypes.byref(rec),
                                     ctypes.byref(ctx), P, WSB, None) == nv.ERR_SHAPE
+
+
+def test_linear_ctx_bytes_and_init():
+    """One-buffer layout of the six layer operands (host bookkeeping only)."""
+    M, K, N = 64, 96, 160
+    nbytes = nv.nvfp4_linear_ctx_bytes(M, K, N)
+    a256 = lambda v: (v + 255) // 256 * 256
+    shapes = [(M, K), (N, K), (K, N), (K, M), (M, N), (N, M)]
+    assert nbytes == sum(a256(r * c // 2) + a256(r * c // 16) + 256 for r, c in shapes)
+    base = 1 << 24
+    ctx = nv.c_linear_ctx()
+    assert nv._lib.nvfp4_linear_ctx_init(ctypes.byref(ctx), base, nbytes, M, K, N) == nv.OK
+    assert (ctx.M, ctx.K, ctx.N) == (M, K, N)
+    end = base
+    for name, (r, c) in zip(("xq", "wq", "wqt", "xqt", "dyq", "dyqt"), shapes):
+        t = getattr(ctx, name)
+        assert (t.rows, t.cols) == (r, c)
+        assert t.codes == end and t.codes % 256 == 0
+        assert t.scales == t.codes + a256(r * c // 2)
+        assert t.global_scale == t.scales + a256(r * c // 16)
+        end = t.global_scale + 256
+    assert end == base + nbytes
+    assert (ctx.wq.scale_mode, ctx.xq.scale_mode) == (nv.SCALE_16X16, nv.SCALE_1X16)
+    f = nv._lib.nvfp4_linear_ctx_init
+    assert f(ctypes.byref(ctx), base, nbytes - 1, M, K, N) == nv.ERR_SHAPE
+    assert f(ctypes.byref(ctx), base + 16, nbytes, M, K, N) == nv.ERR_ALIGN
+    assert f(ctypes.byref(ctx), None, nbytes, M, K, N) == nv.ERR_NULL
+    assert f(ctypes.byref(ctx), base, nbytes, M, K, 40) == nv.ERR_SHAPE
+    with pytest.raises(nv.NVFP4Error):
+        nv.nvfp4_linear_ctx_bytes(0, K, N)

@@ -76,3 +76,30 @@ def test_layer_full_size_sampled(nv):
         Cs, Ss = O.gemm_entries(O.dequant_rows(ra, um), O.dequant_rows(rb, un), im, in_)
         got = out[torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()].float().cpu().numpy()
         assert_gemm_close(got, Cs, Ss, bf16, what)
+
+
+def test_layer_one_buffer_context(nv):
+    """A context laid out in one buffer by nvfp4_linear_ctx_init gives the same
+    operands and outputs, bit for bit, as separately allocated operands."""
+    M, K, N = 512, 640, 384
+    x = W.activations(M, K, seed=W.SEED_X + 60).cuda()
+    w = W.weights(N, K, seed=W.SEED_W + 60).cuda()
+    dy = W.gradients(M, N, seed=W.SEED_DY + 60).cuda()
+    signs = nv.nvfp4_rht_signs_from_seed(W.RHT_SEED)
+    ws = nv.Workspace("cuda")
+    nv.nvfp4_workspace_init(ws)
+    outs = []
+    for ctx in (nv.LinearContext(M, K, N, "cuda"), nv.LinearContext.from_buffer(M, K, N, "cuda")):
+        say("layer ctx", type(ctx).__name__, M, K, N)
+        y = nv.nvfp4_linear_fwd(x, w, ctx, ws, signs, training=True)
+        dx, dw = nv.nvfp4_linear_bwd(dy, ctx, ws, signs, W.SR_SEED)
+        torch.cuda.synchronize()
+        outs.append((ctx, y, dx, dw))
+    (c0, *r0), (c1, *r1) = outs
+    for a, b in zip(r0, r1):
+        assert torch.equal(a, b)
+    for name in ("xq", "wq", "wqt", "xqt", "dyq", "dyqt"):
+        q0, q1 = getattr(c0, name), getattr(c1, name)
+        assert torch.equal(q0.codes_2d(), q1.codes_2d()), name
+        assert torch.equal(q0.scales_2d(), q1.scales_2d()), name
+        assert torch.equal(q0.global_scale, q1.global_scale), name
