@@ -512,8 +512,6 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
   if (recipe->training) {
     NVFP4_TRY(check_out(&ctx->wqt));
     NVFP4_TRY(check_out(&ctx->xqt));
-  } else if (!bf16_fprop) {
-    NVFP4_TRY(check_out(&ctx->wqt));
   }
   if (recipe->rht_signs > 0xFFFFu) return NVFP4_ERR_DTYPE;
   NVFP4_TRY(check_workspace(workspace, ws_bytes));
@@ -527,8 +525,9 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
     set_shape(&ctx->xq, M, K, NVFP4_SCALE_1X16);
     set_shape(&ctx->wq, N, K, wmode);
   }
-  // The BF16 forward of an inference call quantises nothing.
-  const bool want_wt = recipe->training || !bf16_fprop;
+  // W^T (the Dgrad operand) only when training; the BF16 forward of an
+  // inference call quantises nothing.
+  const bool want_wt = recipe->training != 0;
   if (want_wt) set_shape(&ctx->wqt, K, N, wmode);
   NVFP4_HIP(zero_slots(workspace, kSlotXRaw, 3, s));
 
@@ -558,9 +557,11 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
     NVFP4_HIP(launch_quant_tile(dtype, fx, ax, s));
   }
 
-  // W: 16x16 scales, with the transposed copy for Dgrad.  The BF16 forward
-  // keeps only W^T (1x16 along N on its own with no_2d_weights).
-  if (want_wt) {
+  // W: 16x16 scales, with the transposed copy for Dgrad when training.  The
+  // BF16 forward keeps only W^T (1x16 along N on its own with no_2d_weights).
+  const int fw = (bf16_fprop ? 0 : kFRow) | (want_wt ? kFCol : 0) |
+                 (recipe->no_2d_weights ? 0 : kF2D);
+  if (fw & (kFRow | kFCol)) {
     TileArgs aw;
     aw.x = w;
     aw.rows = N;
@@ -568,8 +569,7 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
     aw.ld = K;
     aw.status = ws_word(workspace, kSlotStatus);
     if (!bf16_fprop) aw.row = copy_args(&ctx->wq, workspace, kSlotW, nullptr);
-    aw.col = copy_args(&ctx->wqt, workspace, kSlotW, nullptr);
-    int fw = (bf16_fprop ? 0 : kFRow) | kFCol | (recipe->no_2d_weights ? 0 : kF2D);
+    if (want_wt) aw.col = copy_args(&ctx->wqt, workspace, kSlotW, nullptr);
     NVFP4_HIP(launch_amax(w, dtype, N, K, K, 0, ws_word(workspace, kSlotW), nullptr, s));
     NVFP4_HIP(launch_quant_tile(dtype, fw, aw, s));
   }

@@ -324,11 +324,12 @@ nvfp4_status nvfp4_bf16_gemm(const void* a, const void* b, void* c, int64_t M, i
 /*
  * nvfp4_linear_fwd: forward of one NVFP4 linear layer Y = X W^T [Review s6
  * step 1; Captions Fig. 5].  Quantises X (1x16 RN -> ctx->xq), W (16x16 RN ->
- * ctx->wq and ctx->wqt) and, when recipe->training, (R X)^T (RHT along
- * tokens, RN -> ctx->xqt), then runs the Fprop GEMM.  x [M, K], w [N, K] of
- * `dtype`, dense; y [M, N] bf16.  M, K, N multiples of 16.  With
- * recipe->bf16_fprop only the backward copies (ctx->wqt, and ctx->xqt when
- * training) are made and Fprop is nvfp4_bf16_gemm(x, w).
+ * ctx->wq) and, when recipe->training, the backward copies W^T (-> ctx->wqt)
+ * and (R X)^T (RHT along tokens, RN -> ctx->xqt), then runs the Fprop GEMM.
+ * x [M, K], w [N, K] of `dtype`, dense; y [M, N] bf16.  M, K, N multiples of
+ * 16.  ctx->wqt and ctx->xqt are only needed when training.  With
+ * recipe->bf16_fprop only the backward copies are made (none for inference)
+ * and Fprop is nvfp4_bf16_gemm(x, w).
  */
 nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, int64_t K,
                               int64_t N, int32_t dtype, const nvfp4_recipe* recipe,

@@ -99,3 +99,25 @@ def test_weight_consistency(nv):
     ref_t = O.dequant(O.quantize(np32(w), transpose=True))
     rel_ref = np.linalg.norm(ref - ref_t.T) / np.linalg.norm(ref)
     assert rel == pytest.approx(rel_ref, rel=1e-5)
+
+
+@pytest.mark.parametrize("two_d", [True, False], ids=["2d", "1x16"])
+def test_inference_forward(nv, two_d):
+    """training = False: X and W quantised for Fprop only (no backward copies),
+    Y against the oracle's product of the same operands."""
+    M, K, N = 320, 512, 272
+    x = W.activations(M, K, seed=W.SEED_X + 70)
+    w = W.weights(N, K, seed=W.SEED_W + 70)
+    ws = nv.Workspace("cuda")
+    nv.nvfp4_workspace_init(ws)
+    ctx = nv.LinearContext(M, K, N, "cuda")
+    say("inference forward", M, K, N, two_d)
+    y = nv.nvfp4_linear_fwd(x.cuda(), w.cuda(), ctx, ws, 0, training=False,
+                            no_2d_weights=not two_d)
+    torch.cuda.synchronize()
+    assert nv.nvfp4_device_status(ws) == nv.OK
+    ops = O.linear_operands(np32(x), np32(w), None, O.Recipe(rht_signs=0, weights_2d=two_d))
+    assert_q_equal(ctx.xq, ops["xq"], "xq")
+    assert_q_equal(ctx.wq, ops["wq"], "wq")
+    C, S = O.gemm(ops["xq"], ops["wq"])
+    assert_gemm_close(y.float().cpu().numpy(), C, S, True, "Y inference")
