@@ -876,6 +876,196 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxfp4_gemm_kernel(GemmProblem
   store_tile<OUT_BF16>(acc, 1.0f, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, P.c, P.ldc);
 }
 
+// ------------------------------------------------------------ 128-byte-row slabs
+//
+// LDS-mode loads stream L2-resident data into LDS at about twice the rate when
+// each row segment is 128 bytes rather than 64 (the request rate, not the
+// bytes, is the limit).  This form of the MXFP4 / BF16 kernel therefore takes
+// slabs of 128 bytes per row (256 k of FP4 codes, 64 k of bf16) in two LDS
+// buffers, four K-steps per slab, one barrier per slab:
+//   K-steps 0-2 of slab s (buffer s % 2) run while slab s+1 lands in the
+//   other buffer; then every wave's loads of slab s+1 and LDS reads of slab s
+//   are waited for and a barrier passed; K-step 3 reads K-step 0 of slab s+1
+//   and the loads of slab s+2 go into slab s's buffer.
+// A row's 8 chunks of 16 bytes sit in LDS at slot chunk ^ ((row >> 1) & 7),
+// so the 16 rows a quarter-wave reads cover all 64 banks.  A code load moves
+// 8 rows (lane i: row i / 8, slot i % 8); MXFP4 scale dword d (K-steps 2d,
+// 2d+1) of each row uses the grouped layout of the kernel above.
+constexpr int kWCodeBuf = 256 * 128;                       // one operand tile, one slab
+constexpr int kWACodes = 0, kWBCodes = 2 * kWCodeBuf;       // two buffers each
+constexpr int kWScaleBuf = 2048;                           // 256 rows x 2 dwords
+constexpr int kWAScales = 4 * kWCodeBuf, kWBScales = kWAScales + 2 * kWScaleBuf;
+constexpr int kWLdsBytes = kWBScales + 2 * kWScaleBuf;     // 139264
+
+struct WideLoader {
+  rsrc_t ca, cb, sa, sb;
+  uint32_t vc[2];         // per-lane code offsets for even / odd load index
+  uint32_t vs;            // per-lane scale row offset
+  uint32_t soa, sob;      // code offsets of the wave's first load (tile row 64 w)
+  uint32_t ssa[2], ssb[2];  // scale offsets of the wave's two scale loads
+  uint32_t code_step;     // 8 rows
+  uint32_t lds0;
+  int wave;
+};
+
+// Load n of the wave's share of slab `slab` into buffer u: n = 0..15 codes (A
+// and B alternating, loads 8 w .. 8 w + 7 of each operand), 16..19 MXFP4 scales
+// (A, B, A, B: scale loads 2 w, 2 w + 1 of each operand; load l is dword
+// l / 4, group l % 4).
+__device__ __forceinline__ void wide_load(const WideLoader& L, int slab, int u, int n) {
+  if (n < 16) {
+    const int m = n >> 1, q = 8 * L.wave + m;
+    const uint32_t kc = (uint32_t)slab * 128u;
+    if ((n & 1) == 0)
+      lds_load16(L.ca, L.vc[m & 1], L.soa + m * L.code_step + kc,
+                 L.lds0 + kWACodes + u * kWCodeBuf + q * 1024);
+    else
+      lds_load16(L.cb, L.vc[m & 1], L.sob + m * L.code_step + kc,
+                 L.lds0 + kWBCodes + u * kWCodeBuf + q * 1024);
+  } else if (n < 20) {
+    const int k = (n - 16) >> 1, l = 2 * L.wave + k, d = l >> 2, g = l & 3;
+    const uint32_t ks = (uint32_t)slab * 8u + 4u * (uint32_t)d;
+    const uint32_t dst = (uint32_t)(u * kWScaleBuf + d * 1024 + g * 256);
+    if ((n & 1) == 0)
+      lds_load4(L.sa, L.vs, L.ssa[k] + ks, L.lds0 + kWAScales + dst);
+    else
+      lds_load4(L.sb, L.vs, L.ssb[k] + ks, L.lds0 + kWBScales + dst);
+  }
+}
+
+struct WideDma {
+  const WideLoader& L;
+  int slab, u, nloads;
+  __device__ __forceinline__ void operator()(int G) {
+    if (G < nloads) wide_load(L, slab, u, G);
+    if (G == 15)
+      for (int n = 16; n < nloads; ++n) wide_load(L, slab, u, n);
+  }
+};
+
+// LDS reads of K-step J's fragments of the slab in buffer u (chunks 0..7),
+// with D >= 0 also scale dword D (chunks 8, 9).
+template <int D>
+struct WideMem {
+  const uint8_t* lds;
+  uint32_t rca, rcb;  // per-lane code address of row block 0 for this K-step
+  uint32_t rsa, rsb;  // per-lane scale group address
+  int u;
+  MxRaw& r;
+  uint4& sa;
+  uint4& sb;
+  __device__ __forceinline__ void operator()(int idx) {
+    if (idx < 4)
+      r.ca[idx] = *reinterpret_cast<const uint4*>(lds + rca + u * kWCodeBuf + idx * 4096);
+    else if (idx < 8)
+      r.cb[idx - 4] = *reinterpret_cast<const uint4*>(lds + rcb + u * kWCodeBuf + (idx - 4) * 4096);
+    else if (D >= 0 && idx == 8)
+      sa = *reinterpret_cast<const uint4*>(lds + rsa + u * kWScaleBuf + D * 1024);
+    else if (D >= 0 && idx == 9)
+      sb = *reinterpret_cast<const uint4*>(lds + rsb + u * kWScaleBuf + D * 1024);
+  }
+};
+
+template <bool OUT_BF16, int FMT>
+__global__ __launch_bounds__(kGemmThreads, 1) void wide_gemm_kernel(GemmProblem P) {
+  constexpr bool MX = FMT == kFmtMx;
+  constexpr int kSlabElems = MX ? 256 : 64;      // k per slab (128 bytes per row)
+  constexpr int kLoads = MX ? 20 : 16;
+  __shared__ __align__(16) uint8_t lds[kWLdsBytes];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int prob, local, tm, tn;
+  tile_of2(P.tiles_m * P.tiles_n, 0, &prob, &local);
+  group_tile(local, P.tiles_m, P.tiles_n, &tm, &tn);
+  const GemmOperand a = P.a, b = P.b;
+  const int64_t K = P.K, m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+  const int ns = (int)(K / kSlabElems);
+  const uint32_t row_bytes = (uint32_t)(MX ? K / 2 : K * 2), srow_bytes = (uint32_t)(K / 32);
+
+  WideLoader L;
+  L.ca = make_rsrc(a.codes, (uint32_t)(a.rows * row_bytes));
+  L.cb = make_rsrc(b.codes, (uint32_t)(b.rows * row_bytes));
+  L.sa = make_rsrc(MX ? a.scales : a.codes, MX ? (uint32_t)(a.rows * srow_bytes) : 0u);
+  L.sb = make_rsrc(MX ? b.scales : b.codes, MX ? (uint32_t)(b.rows * srow_bytes) : 0u);
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+    L.vc[p] = (uint32_t)(lane >> 3) * row_bytes +
+              16u * (uint32_t)((lane & 7) ^ (4 * p + (lane >> 4)));
+  L.code_step = 8u * row_bytes;
+  L.soa = (uint32_t)(m0 + 64 * wave) * row_bytes;
+  L.sob = (uint32_t)(n0 + 64 * wave) * row_bytes;
+  L.vs = (uint32_t)(32 * (lane & 3) + (lane >> 2)) * srow_bytes;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int g = (2 * wave + k) & 3;
+    const int64_t tr = 128 * (g >> 1) + 16 * (g & 1);
+    L.ssa[k] = (uint32_t)(m0 + tr) * srow_bytes;
+    L.ssb[k] = (uint32_t)(n0 + tr) * srow_bytes;
+  }
+  L.lds0 = (uint32_t)(uintptr_t)lds;
+  L.wave = wave;
+
+  const int h = lane >> 5, rl = lane & 31, sw = (rl >> 1) & 7;
+  uint32_t rca[4], rcb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t slot = (uint32_t)((2 * j + h) ^ sw);
+    rca[j] = kWACodes + (uint32_t)(wm * 128 + rl) * 128 + 16 * slot;
+    rcb[j] = kWBCodes + (uint32_t)(wn * 128 + rl) * 128 + 16 * slot;
+  }
+  const uint32_t rsa = kWAScales + (uint32_t)wm * 512 + (uint32_t)rl * 16;
+  const uint32_t rsb = kWBScales + (uint32_t)wn * 512 + (uint32_t)rl * 16;
+
+  float16_t acc[4][4];
+  zero_acc(acc);
+#pragma unroll
+  for (int n = 0; n < kLoads; ++n) wide_load(L, 0, 0, n);
+#pragma unroll
+  for (int n = 0; n < kLoads; ++n) wide_load(L, ns > 1 ? 1 : 0, 1, n);
+  wait_vmcnt<kLoads>();
+  __builtin_amdgcn_s_barrier();
+
+  MxRaw r0, r1;
+  uint4 sa0 = make_uint4(0, 0, 0, 0), sb0 = sa0, sa1 = sa0, sb1 = sa0;
+  {
+    WideMem<MX ? 0 : -1> first{lds, rca[0], rcb[0], rsa, rsb, 0, r0, sa0, sb0};
+#pragma unroll
+    for (int idx = 0; idx < 10; ++idx) first(idx);
+  }
+  for (int s = 0; s < ns; ++s) {
+    const int u = s & 1;
+    NoMem none;
+    {
+      WideMem<MX ? 1 : -1> m{lds, rca[1], rcb[1], rsa, rsb, u, r1, sa1, sb1};
+      mx_kstep<FMT, 0>(acc, r0, sa0, sb0, h, m, none);
+    }
+    {
+      WideMem<-1> m{lds, rca[2], rcb[2], rsa, rsb, u, r0, sa1, sb1};
+      mx_kstep<FMT, 1>(acc, r1, sa0, sb0, h, m, none);
+    }
+    {
+      WideMem<-1> m{lds, rca[3], rcb[3], rsa, rsb, u, r1, sa1, sb1};
+      mx_kstep<FMT, 0>(acc, r0, sa1, sb1, h, m, none);
+    }
+    // slab s+1 landed for this wave and its reads of buffer u are done; then
+    // for every wave
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    {
+      WideMem<MX ? 0 : -1> m{lds, rca[0], rcb[0], rsa, rsb, u ^ 1, r0, sa0, sb0};
+      WideDma dma{L, s + 2 < ns ? s + 2 : 0, u, kLoads};
+      // sa1/sb1 still hold slab s's dword 1 for this K-step; sa0/sb0 are
+      // overwritten with slab s+1's dword 0 by the reads (chunks 8, 9)
+      const uint4 ka = sa1, kb = sb1;
+      mx_kstep<FMT, 1>(acc, r1, ka, kb, h, m, dma);
+    }
+  }
+  wait_vmcnt<0>();
+
+  store_tile<OUT_BF16>(acc, 1.0f, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, P.c, P.ldc);
+}
+
 // ------------------------------------------------------------ launch
 
 // Shapes the slab kernel takes: at least three slabs (the prologue loads
@@ -951,9 +1141,24 @@ hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, vo
   return launch_direct(p, bf16, s);
 }
 
+#ifndef NVFP4_WIDE_SLABS
+#define NVFP4_WIDE_SLABS 1
+#endif
+
+template <int FMT>
+static hipError_t launch_wide(const GemmProblem& p, int c_dtype, hipStream_t s) {
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kGemmThreads);
+  if (c_dtype == kDtypeBF16)
+    hipLaunchKernelGGL((wide_gemm_kernel<true, FMT>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((wide_gemm_kernel<false, FMT>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, void* c,
                           int c_dtype, int64_t ldc, hipStream_t s) {
   const GemmProblem p = make_problem(a, b, K, c, ldc);
+  if (NVFP4_WIDE_SLABS && K % 256 == 0) return launch_wide<kFmtMx>(p, c_dtype, s);
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kGemmThreads);
   if (c_dtype == kDtypeBF16)
     hipLaunchKernelGGL((mxfp4_gemm_kernel<true, kFmtMx>), grid, block, 0, s, p);
@@ -967,6 +1172,7 @@ hipError_t launch_bf16_gemm(const void* a, int64_t M, const void* b, int64_t N, 
   GemmOperand oa{static_cast<const uint8_t*>(a), nullptr, nullptr, M, 0};
   GemmOperand ob{static_cast<const uint8_t*>(b), nullptr, nullptr, N, 0};
   const GemmProblem p = make_problem(oa, ob, K, c, ldc);
+  if (NVFP4_WIDE_SLABS && K % 64 == 0) return launch_wide<kFmtBf16>(p, c_dtype, s);
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kGemmThreads);
   if (c_dtype == kDtypeBF16)
     hipLaunchKernelGGL((mxfp4_gemm_kernel<true, kFmtBf16>), grid, block, 0, s, p);
