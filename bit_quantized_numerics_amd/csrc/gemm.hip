@@ -668,6 +668,210 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_lds_kernel(GemmProblem p0, Ge
     store_tile<OUT1_BF16>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
 }
 
+// ------------------------------------------------------------ 128-byte-row NVFP4 slabs
+//
+// The slab kernel with slabs of 256 k: 128 bytes of codes and 16 bytes of 1x16
+// scales per row (LDS-mode loads stream twice as fast with 128-byte row
+// segments as with 64), two LDS buffers, four K-steps and one barrier per
+// slab, in the order of the 128-byte-row MXFP4 / BF16 kernel below: K-steps
+// 0-2 of slab s, then (slab s+1 landed and slab s's reads done in every
+// wave) K-step 3 reading K-step 0 of slab s+1 while slab s+2 loads into slab
+// s's buffer.  Codes of row r sit at chunk slot c ^ ((r >> 1) & 7).  Scales:
+// per buffer and operand, tile half H, lane row rl (0..31) and K-step j, the
+// 16 bytes at H * 2048 + rl * 64 + 16 * (j ^ ((rl >> 2) & 3)) hold the K-step's
+// scale dword of rows 128 H + 32 i + rl, i = 0..3, so one 16-byte read gives
+// a lane all four row blocks' scales and a quarter-wave's reads cover all
+// banks.  Scale load L (0..15 per operand, dword loads) fills 256 bytes: tile
+// half L / 8, lane rows 4 (L % 8) + l / 16, slot (l / 4) % 4, row block l % 4
+// for lane l.  NW = 4 only.
+constexpr int kXCodeBuf = 256 * 128, kXScaleBuf = 256 * 16;
+constexpr int kXACodes = 0, kXBCodes = 2 * kXCodeBuf;
+constexpr int kXAScales = 4 * kXCodeBuf, kXBScales = kXAScales + 2 * kXScaleBuf;
+static_assert(kXBScales + 2 * kXScaleBuf == kLdsBytes, "LDS map");
+constexpr int kXLoads = 24;  // per wave and slab: 8 + 8 code loads, 4 + 4 scale loads
+
+struct XSlabLoader {
+  rsrc_t ca, cb, sa, sb;
+  uint32_t vc[2];            // per-lane code offsets for even / odd load index
+  uint32_t vsa[4], vsb[4];   // per-lane scale offsets of the wave's scale loads
+  uint32_t soa, sob;         // code offsets of the wave's first load (tile row 64 w)
+  uint32_t ssa[4], ssb[4];   // scale offsets of the wave's scale loads
+  uint32_t code_step;        // 8 rows
+  uint32_t lds0;
+  int wave;
+};
+
+__device__ __forceinline__ void xslab_load(const XSlabLoader& L, int slab, int u, int n) {
+  if (n < 16) {
+    const int m = n >> 1, q = 8 * L.wave + m;
+    const uint32_t kc = (uint32_t)slab * 128u;
+    if ((n & 1) == 0)
+      lds_load16(L.ca, L.vc[m & 1], L.soa + m * L.code_step + kc,
+                 L.lds0 + kXACodes + u * kXCodeBuf + q * 1024);
+    else
+      lds_load16(L.cb, L.vc[m & 1], L.sob + m * L.code_step + kc,
+                 L.lds0 + kXBCodes + u * kXCodeBuf + q * 1024);
+  } else if (n < kXLoads) {
+    const int k = (n - 16) >> 1, l = 4 * L.wave + k;
+    const uint32_t ks = (uint32_t)slab * 16u;
+    if ((n & 1) == 0)
+      lds_load4(L.sa, L.vsa[k], L.ssa[k] + ks, L.lds0 + kXAScales + u * kXScaleBuf + l * 256);
+    else
+      lds_load4(L.sb, L.vsb[k], L.ssb[k] + ks, L.lds0 + kXBScales + u * kXScaleBuf + l * 256);
+  }
+}
+
+// The slab's loads over the 16 chunks of a sub-step (two per chunk first).
+struct XSlabDma {
+  const XSlabLoader& L;
+  int slab, u;
+  __device__ __forceinline__ void operator()(int G) {
+    xslab_load(L, slab, u, G);
+    if (G < kXLoads - 16) xslab_load(L, slab, u, 16 + G);
+  }
+};
+
+// Per-lane LDS read addresses: codes of row block 0 and the scale group, per K-step.
+struct XSlabReader {
+  uint32_t ca[4], cb[4], sa[4], sb[4];
+};
+
+template <int J>
+struct XSlabMem {
+  const uint8_t* lds;
+  const XSlabReader& R;
+  int u;
+  StepRawT<4>& r;
+  __device__ __forceinline__ void operator()(int idx) {
+    if (idx < 4) {
+      r.ca[idx] = *reinterpret_cast<const uint4*>(lds + R.ca[J] + u * kXCodeBuf + idx * 4096);
+    } else if (idx < 8) {
+      r.cb[idx - 4] =
+          *reinterpret_cast<const uint4*>(lds + R.cb[J] + u * kXCodeBuf + (idx - 4) * 4096);
+    } else if (idx == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + R.sa[J] + u * kXScaleBuf);
+      r.sa[0] = v.x; r.sa[1] = v.y; r.sa[2] = v.z; r.sa[3] = v.w;
+    } else if (idx == 9) {
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + R.sb[J] + u * kXScaleBuf);
+      r.sb[0] = v.x; r.sb[1] = v.y; r.sb[2] = v.z; r.sb[3] = v.w;
+    }
+  }
+};
+
+template <bool OUT0_BF16, bool OUT1_BF16>
+__global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmProblem p0, GemmProblem p1) {
+  constexpr int NB = 4;
+  __shared__ __align__(16) uint8_t lds[kLdsBytes];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int prob, local, tm, tn;
+  tile_of2(p0.tiles_m * p0.tiles_n, p1.tiles_m * p1.tiles_n, &prob, &local);
+  const GemmProblem& P = prob ? p1 : p0;
+  const GemmOperand a = P.a, b = P.b;
+  const int64_t K = P.K;
+  group_tile(local, P.tiles_m, P.tiles_n, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+  const int ns = (int)(K / 256);
+  const uint32_t row_bytes = (uint32_t)(K / 2), srow_bytes = (uint32_t)(K / 16);
+
+  XSlabLoader L;
+  {
+    const int sha = a.scale_shift, shb = b.scale_shift;
+    const int64_t srows_a = sha ? (a.rows + 15) >> 4 : a.rows;
+    const int64_t srows_b = shb ? (b.rows + 15) >> 4 : b.rows;
+    L.ca = make_rsrc(a.codes, (uint32_t)(a.rows * row_bytes));
+    L.cb = make_rsrc(b.codes, (uint32_t)(b.rows * row_bytes));
+    L.sa = make_rsrc(a.scales, (uint32_t)(srows_a * srow_bytes));
+    L.sb = make_rsrc(b.scales, (uint32_t)(srows_b * srow_bytes));
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      L.vc[p] = (uint32_t)(lane >> 3) * row_bytes +
+                16u * (uint32_t)((lane & 7) ^ (4 * p + (lane >> 4)));
+    L.code_step = 8u * row_bytes;
+    L.soa = (uint32_t)(m0 + 64 * wave) * row_bytes;
+    L.sob = (uint32_t)(n0 + 64 * wave) * row_bytes;
+    // scale load l = 4 w + k: tile half H = l / 8, g = l % 8; lane row part
+    // 32 (i % 4) + i / 16, K-step ((i / 4) % 4) ^ (g % 4); row = 128 H + 4 g +
+    // lane part (the 16x16 shift splits as 8 H + g / 4 + 2 (i % 4))
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int l = 4 * wave + k, H = l >> 3, g = l & 7;
+      const uint32_t j = (uint32_t)(((lane >> 2) & 3) ^ (g & 3));
+      const uint32_t lane_row = (uint32_t)(32 * (lane & 3) + (lane >> 4));
+      const uint32_t lane_row16 = (uint32_t)(2 * (lane & 3));
+      L.vsa[k] = (sha ? lane_row16 : lane_row) * srow_bytes + 4u * j;
+      L.vsb[k] = (shb ? lane_row16 : lane_row) * srow_bytes + 4u * j;
+      const int64_t tr = 128 * H + 4 * g;
+      L.ssa[k] = (uint32_t)(sha ? (m0 >> 4) + 8 * H + (g >> 2) : m0 + tr) * srow_bytes;
+      L.ssb[k] = (uint32_t)(shb ? (n0 >> 4) + 8 * H + (g >> 2) : n0 + tr) * srow_bytes;
+    }
+    L.lds0 = (uint32_t)(uintptr_t)lds;
+    L.wave = wave;
+  }
+
+  const int h = lane >> 5, rl = lane & 31;
+  const int brow0 = 128 * wn;
+  XSlabReader R;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t slot = (uint32_t)((2 * j + h) ^ ((rl >> 1) & 7));
+    R.ca[j] = kXACodes + (uint32_t)(wm * 128 + rl) * 128 + 16 * slot;
+    R.cb[j] = kXBCodes + (uint32_t)(brow0 + rl) * 128 + 16 * slot;
+    const uint32_t sslot = (uint32_t)(j ^ ((rl >> 2) & 3));
+    R.sa[j] = kXAScales + (uint32_t)wm * 2048 + (uint32_t)rl * 64 + 16 * sslot;
+    R.sb[j] = kXBScales + (uint32_t)wn * 2048 + (uint32_t)rl * 64 + 16 * sslot;
+  }
+  const uint32_t sel = h ? 0x0C030C02u : 0x0C010C00u;
+
+  float16_t acc[4][NB];
+  zero_acc(acc);
+#pragma unroll
+  for (int n = 0; n < kXLoads; ++n) xslab_load(L, 0, 0, n);
+#pragma unroll
+  for (int n = 0; n < kXLoads; ++n) xslab_load(L, ns > 1 ? 1 : 0, 1, n);
+  wait_vmcnt<kXLoads>();
+  __builtin_amdgcn_s_barrier();
+
+  StepRawT<NB> r0, r1;
+  {
+    XSlabMem<0> first{lds, R, 0, r0};
+#pragma unroll
+    for (int idx = 0; idx < 10; ++idx) first(idx);
+  }
+  FragsT<NB> f;
+  uint32_t dp[4 + NB];
+  first_frags(r0, sel, f, dp);
+  for (int s = 0; s < ns; ++s) {
+    const int u = s & 1;
+    {
+      XSlabMem<1> m{lds, R, u, r1};
+      k_step(acc, f, dp, r0, r1, true, sel, m);
+    }
+    {
+      XSlabMem<2> m{lds, R, u, r0};
+      k_step(acc, f, dp, r1, r0, true, sel, m);
+    }
+    {
+      XSlabMem<3> m{lds, R, u, r1};
+      k_step(acc, f, dp, r0, r1, true, sel, m);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): slab s+1, reads of slab s
+    __builtin_amdgcn_s_barrier();        // ... in every wave: buffer u is free
+    {
+      XSlabMem<0> m{lds, R, u ^ 1, r0};
+      k_step(acc, f, dp, r1, r0, true, sel, m, XSlabDma{L, s + 2 < ns ? s + 2 : 0, u});
+    }
+  }
+  wait_vmcnt<0>();  // no LDS-mode load may outlive the workgroup's LDS
+
+  const float gab = (*a.global) * (*b.global) * 65536.0f;
+  if (OUT0_BF16 == OUT1_BF16 || prob == 0)
+    store_tile<OUT0_BF16>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
+  else
+    store_tile<OUT1_BF16>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
+}
+
 // ------------------------------------------------------------ MXFP4 / BF16 kernel
 //
 // The comparator format [Review "secret weapon" items 1-2; Captions Fig. 6]:
@@ -1100,11 +1304,22 @@ static bool slab_ok(const GemmProblem& p) {
 #endif
 constexpr int kSlabWaves = NVFP4_SLAB_WAVES;
 
+#ifndef NVFP4_WIDE_SLABS
+#define NVFP4_WIDE_SLABS 1
+#endif
+
+// 256-k slabs when every problem's K allows (problem 1 may be empty).
 template <bool OUT0, bool OUT1>
 static hipError_t launch_slab(const GemmProblem& p0, const GemmProblem& p1, hipStream_t s) {
   const int n = p0.tiles_m * p0.tiles_n + p1.tiles_m * p1.tiles_n;
-  hipLaunchKernelGGL((gemm_lds_kernel<OUT0, OUT1, kSlabWaves>), dim3((unsigned)n),
-                     dim3(64 * kSlabWaves), 0, s, p0, p1);
+  const bool wide = NVFP4_WIDE_SLABS && kSlabWaves == 4 && p0.K % 256 == 0 &&
+                    (p1.tiles_m * p1.tiles_n == 0 || p1.K % 256 == 0);
+  if (wide)
+    hipLaunchKernelGGL((gemm_wide_kernel<OUT0, OUT1>), dim3((unsigned)n), dim3(256), 0, s, p0,
+                       p1);
+  else
+    hipLaunchKernelGGL((gemm_lds_kernel<OUT0, OUT1, kSlabWaves>), dim3((unsigned)n),
+                       dim3(64 * kSlabWaves), 0, s, p0, p1);
   return hipGetLastError();
 }
 
@@ -1140,10 +1355,6 @@ hipError_t launch_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K, vo
   if (slab_ok(p)) return launch_slab_dt(p, bf16, no_problem(), bf16, s);
   return launch_direct(p, bf16, s);
 }
-
-#ifndef NVFP4_WIDE_SLABS
-#define NVFP4_WIDE_SLABS 1
-#endif
 
 template <int FMT>
 static hipError_t launch_wide(const GemmProblem& p, int c_dtype, hipStream_t s) {
