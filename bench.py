@@ -44,8 +44,8 @@ BYTES_2D = 2.0 + 2 * (0.5 + 1.0 / 256)
 # 1 GiB device copy reads back), averaged over the single Fprop, Dgrad and
 # Wgrad launches: 1072.7, 875.8 and 1286.5 MB.  Valid only for the kernel
 # source it was measured on (profiles/hbm_traffic_gemm_quantize_*.md).
-GEMM_TRAFFIC = {"source_sha1": "eadad7b74f082e746c07128b72f2ce26293f7e98",
-                "bytes_per_launch": 1078.4e6}
+GEMM_TRAFFIC = {"source_sha1": "2d422a70b368d9fc27e77ae03c4a4b897507db9b",
+                "bytes_per_launch": 1078.1e6}
 
 
 def _gemm_source_sha1() -> str:
