@@ -330,6 +330,18 @@ def main():
     out["weight_consistency"] = weight_consistency(nv, w, ws)
     out["rht_sizes"] = rht_sizes(nv, x, ws, max(3, args.steps // 2))
     out["bf16_fprop"] = bf16_fprop(nv, x, w, ctx, ws, signs, max(3, args.steps // 2))
+    # the compute ceiling the card holds under a sustained fp16 MFMA load (no
+    # memory traffic), next to the datasheet peak used in `roofline`
+    nv.nvfp4_peak_mfma_f16(1000)
+    mfma_loop = nv.nvfp4_peak_mfma_f16(5000)
+    mfma_const = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0)
+    out["measured_ceiling"] = {
+        "mfma_f16_loop_TFLOPs": round(mfma_loop, 1),
+        "mfma_f16_loop_constant_operands_TFLOPs": round(mfma_const, 1),
+        "gemm_frac_of_loop": round(achieved / mfma_loop, 4),
+        "note": "fp16 MFMA-only loop shaped like the GEMM's (16 accumulators per wave, 4 VALU per "
+                "MFMA), random-looking operands changing every iteration; and the same "
+                "instructions on constant operands"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

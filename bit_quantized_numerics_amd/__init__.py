@@ -79,6 +79,7 @@ _SIGS = {
     "nvfp4_rht_signs128_from_seed": (None, [_u64, ctypes.POINTER(_u32)]),
     "nvfp4_gemm": (_i32, [_T, _T, _vp, _i32, _i64, _vp, _sz, _vp]),
     "nvfp4_bf16_gemm": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _vp]),
+    "nvfp4_peak_mfma_f16": (_i32, [_i32, _u32, _vp, ctypes.POINTER(ctypes.c_double), _vp]),
     "nvfp4_linear_ctx_bytes": (_i32, [_i64, _i64, _i64, ctypes.POINTER(_sz)]),
     "nvfp4_linear_ctx_init": (_i32, [ctypes.POINTER(c_linear_ctx), _vp, _sz, _i64, _i64, _i64]),
     "nvfp4_linear_fwd": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, ctypes.POINTER(c_recipe),
@@ -331,6 +332,21 @@ def nvfp4_bf16_gemm(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.float32,
                                 ctypes.c_void_p(c.data_ptr()), M, N, K, _dtype_code(c), _ld(c),
                                 _stream(a.device)), "nvfp4_bf16_gemm")
     return c
+
+
+def nvfp4_peak_mfma_f16(iters: int, toggle_mask: int = 0x87FF87FF, device="cuda") -> float:
+    """Time the fp16 MFMA loop on the current stream; returns TFLOP/s."""
+    sink = torch.empty(2048, dtype=torch.float32, device=device)
+    flops = ctypes.c_double(0.0)
+    stream = torch.cuda.current_stream(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    _check(_lib.nvfp4_peak_mfma_f16(iters, toggle_mask, ctypes.c_void_p(sink.data_ptr()),
+                                    ctypes.byref(flops),
+                                    _stream(torch.device(device))), "nvfp4_peak_mfma_f16")
+    e1.record(stream)
+    e1.synchronize()
+    return flops.value / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 def nvfp4_linear_ctx_bytes(M: int, K: int, N: int) -> int:

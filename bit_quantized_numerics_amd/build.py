@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "peak.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

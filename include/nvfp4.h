@@ -349,6 +349,22 @@ nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* c
                               const nvfp4_recipe* recipe, void* workspace, size_t ws_bytes,
                               void* stream);
 
+/*
+ * nvfp4_peak_mfma_f16: measurement helper, not part of the layer.  Enqueues
+ * an fp16 MFMA loop shaped like the GEMM's inner loop
+ * (v_mfma_f32_32x32x16_f16, FP32 accumulation, one wave per SIMD, no memory
+ * traffic, random-looking operands that change every iteration) of `iters`
+ * iterations and returns in *flops the floating-point operations it
+ * performs; timing it on the stream gives the compute ceiling the card holds
+ * under sustained MFMA load, next to the datasheet peak.  toggle_mask picks
+ * the operand bits that change (ANDed with 0x87FF87FF, the sign and mantissa
+ * bits of two f16): 0 runs the same instructions on constant operands.
+ * sink: a device buffer of 2048 floats the kernel may write (it does not in
+ * practice).
+ */
+nvfp4_status nvfp4_peak_mfma_f16(int32_t iters, uint32_t toggle_mask, float* sink, double* flops,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -215,3 +215,11 @@ def test_linear_ctx_bytes_and_init():
     assert f(ctypes.byref(ctx), base, nbytes, M, K, 40) == nv.ERR_SHAPE
     with pytest.raises(nv.NVFP4Error):
         nv.nvfp4_linear_ctx_bytes(0, K, N)
+
+
+def test_peak_helper_argument_errors():
+    flops = ctypes.c_double(0)
+    f = nv._lib.nvfp4_peak_mfma_f16
+    assert f(100, 0, None, ctypes.byref(flops), None) == nv.ERR_NULL
+    assert f(100, 0, P, None, None) == nv.ERR_NULL
+    assert f(0, 0, P, ctypes.byref(flops), None) == nv.ERR_SHAPE

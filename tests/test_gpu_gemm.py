@@ -164,3 +164,12 @@ def test_full_wgrad_sampled(nv, ws):
     ra = O.quantize(np32(dy), transpose=True, rht=True, signs=s, sr=True, seed=W.SR_SEED, stream=1)
     rb = O.quantize(np32(x), transpose=True, rht=True, signs=s)
     _sampled_check(nv, qa, qb, ra, rb, torch.float32, "wgrad")
+
+
+def test_mfma_loop_ceiling(nv):
+    """The measurement helper runs and reports a plausible fp16 MFMA rate
+    (above any GEMM here, below the datasheet peak)."""
+    say("mfma loop ceiling")
+    nv.nvfp4_peak_mfma_f16(200)
+    tf = nv.nvfp4_peak_mfma_f16(2000)
+    assert 500.0 < tf < 2600.0, tf
