@@ -61,9 +61,11 @@ def test_layer_dw_tracks_unquantised_gradient(nv):
 
 
 @pytest.mark.slow
-def test_layer_full_size_sampled(nv):
-    """The benchmarked workload: 8192 tokens, 5120 -> 20480."""
-    M, K, N = W.LAYER_M, W.LAYER_K, W.LAYER_N
+@pytest.mark.parametrize("M", [W.LAYER_M, 2 * W.LAYER_M])
+def test_layer_full_size_sampled(nv, M):
+    """The FFN up-projection 5120 -> 20480 at 8192 tokens (the benchmarked
+    workload) and at 16384 tokens: every operand bit-exact, sampled outputs."""
+    K, N = W.LAYER_K, W.LAYER_N
     ctx, ops, y, dx, dw, _ = _run_layer(nv, M, K, N)
     g = np.random.default_rng(5)
     for out, (a, b), bf16, what in ((y, ("xq", "wq"), True, "Y"), (dx, ("dyq", "wqt"), True, "dX"),
