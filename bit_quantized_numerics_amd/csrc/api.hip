@@ -43,6 +43,8 @@ inline uint32_t* ws_word(void* ws, int slot) {
 inline hipError_t zero_slots(void* ws, int slot, int n, hipStream_t s) {
   return launch_zero_words(ws_word(ws, slot), n * kAmaxRegionWords, s);
 }
+// Largest source row count: the stats kernel's grid has one y index per 128 rows.
+constexpr int64_t kMaxRows = (int64_t)65535 * 128;
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t elem_bytes(int dtype) { return dtype == NVFP4_BF16 ? 2 : 4; }
 
@@ -58,7 +60,7 @@ nvfp4_status check_source(const void* x, int32_t dtype, int64_t rows, int64_t co
   if (!x) return NVFP4_ERR_NULL;
   if (dtype != NVFP4_F32 && dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (rows <= 0 || cols <= 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (rows > (int64_t)65535 * 256) return NVFP4_ERR_SHAPE;  // grid y limit
+  if (rows > kMaxRows) return NVFP4_ERR_SHAPE;  // grid y of the 128-row stats tiles
   if (ld < cols) return NVFP4_ERR_SHAPE;
   // a 256-row tile of the source must be addressable with 32-bit offsets
   if (ld * (int64_t)elem_bytes(dtype) * 256 >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
@@ -405,7 +407,7 @@ nvfp4_status nvfp4_rht16(const void* x, float* y, int32_t in_dtype, int64_t rows
   if (rows <= 0 || cols <= 0 || ld < cols) return NVFP4_ERR_SHAPE;
   if (axis == 1 && cols % 16 != 0) return NVFP4_ERR_SHAPE;
   if (axis == 0 && (rows % 16 != 0 || cols % 8 != 0)) return NVFP4_ERR_SHAPE;
-  if (rows > (int64_t)65535 * 256) return NVFP4_ERR_SHAPE;
+  if (rows > kMaxRows) return NVFP4_ERR_SHAPE;
   if (ld * (int64_t)elem_bytes(in_dtype) * 256 >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, 16) || (ld * (int64_t)elem_bytes(in_dtype)) % 16 != 0)
     return NVFP4_ERR_ALIGN;

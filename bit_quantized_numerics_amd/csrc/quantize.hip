@@ -5,11 +5,10 @@
 // by numbered section; [Captions] = that paper's figure-caption list.
 //
 // Work decomposition.  Every kernel walks the source matrix x [rows, cols]
-// (row-major, cols contiguous) in tiles of 256 rows x 256 columns; each of
-// the 512 threads of a workgroup owns one 16-row x 8-column patch (32 patch
-// columns x 16 patch rows, so a wave covers two 16-row strips of 512 bytes
-// per row).  That
-// patch shape serves every block geometry of the layer:
+// (row-major, cols contiguous) in tiles of 256 columns and 128 or 256 rows;
+// each thread of a workgroup owns one 16-row x 8-column patch (32 patch
+// columns x 8 or 16 patch rows, so a wave covers two 16-row strips of 512
+// bytes per row).  That patch shape serves every block geometry of the layer:
 //   - a 1x16 block along cols is one row of the patch plus the neighbouring
 //     lane's row (lane ^ 1 holds the other 8 columns);
 //   - a 1x16 block along rows (the column-wise copy the backward GEMMs need,
@@ -18,9 +17,10 @@
 //   - a 16x16 weight tile is the patch plus its neighbour lane's patch.
 // Reads are 16-byte loads, 16 per thread in flight.  Every row of the row-wise
 // copy is written as 128 contiguous bytes per tile.  Each 16-element column
-// block of the column-wise copy is one 8-byte store; the 16 row strips of a
-// workgroup fill each 128-byte output line within the same workgroup, so the
-// L2 merges them (an LDS transpose stage only added bank-conflicted stores).
+// block of the column-wise copy is one 8-byte store; the 16 row strips of 256
+// rows fill each 128-byte output line within one workgroup, or within two
+// workgroups that run back to back on one XCD, so its L2 merges them (an LDS
+// transpose stage only added bank-conflicted stores).
 //
 // Tensor amax.  Each stats workgroup reduces its tile in LDS and adds one
 // atomicMax to one of kAmaxSlots words (chosen by workgroup id, each slot on
@@ -203,14 +203,42 @@ __device__ __forceinline__ bool copy_scales(const uint32_t* amax, uint32_t* stat
   return true;
 }
 
+// Emit tile rows per flag set: 128 (256 threads), or 256 (512 threads) for
+// the 16x16 weight copies.  The smaller tile gives the activation and
+// gradient tensors several workgroups per CU; the weight kernel does little
+// arithmetic per byte, and there the per-workgroup set-up of the larger
+// tile's half as many workgroups measured faster.
+constexpr int emit_rows(int F) { return (F & kF2D) ? 256 : 128; }
+
+// Workgroup -> emit tile.  With 128-row tiles, the two tiles of a 256-row
+// pair write the two halves of every 128-byte line of the column-wise copy,
+// so they are given workgroups b and b + 8: workgroups go round-robin over
+// the 8 XCDs, so both run on the same XCD, one after the other, and its L2
+// merges the halves before the line is written back.  Pair p (column tile
+// fastest) is taken by workgroups 16 (p / 8) + p % 8 and that + 8.  Returns
+// false for the workgroups past the last tile (the grid is rounded up to 16).
+template <int TR>
+__device__ __forceinline__ bool emit_tile(int64_t rows, int64_t cols, int64_t* tile_r0,
+                                          int64_t* tile_c0) {
+  const int64_t gx = (cols + kTileC - 1) / kTileC, gy = (rows + TR - 1) / TR;
+  const int64_t b = blockIdx.x, p = (b >> 4) * 8 + (b & 7);
+  const int64_t ty = 2 * (p / gx) + ((b >> 3) & 1), tx = p % gx;
+  if (ty >= gy) return false;
+  *tile_r0 = ty * TR;
+  *tile_c0 = tx * kTileC;
+  return true;
+}
+
 template <typename TIn, int F>
-__global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
+__global__ __launch_bounds__(2 * emit_rows(F)) void quant_tile_kernel(TileArgs a) {
+  constexpr int TR = emit_rows(F);
   constexpr bool ROW = F & kFRow, COL = F & kFCol, TWO_D = F & kF2D, RHT = F & kFRht;
   constexpr bool SR_ROW = F & kFSrRow, SR_COL = F & kFSrCol;
 
   const int t = threadIdx.x, cg = t & 31, rs = t >> 5;
   const int64_t rows = a.rows, cols = a.cols;
-  const int64_t tile_r0 = (int64_t)blockIdx.y * kTileR, tile_c0 = (int64_t)blockIdx.x * kTileC;
+  int64_t tile_r0, tile_c0;
+  if (!emit_tile<TR>(rows, cols, &tile_r0, &tile_c0)) return;  // uniform across the workgroup
   const int64_t r0 = tile_r0 + rs * 16, c0 = tile_c0 + cg * 8;
   const bool valid = r0 < rows && c0 < cols;
 
@@ -225,14 +253,14 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
       do_col = copy_scales(a.col.amax, a.status, &tc);
     }
   }
-  if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
+  if (blockIdx.x == 0 && t == 0) {
     if (do_row) *a.row.global = tr.g;
     if (do_col && a.col.global) *a.col.global = tc.g;
   }
   if (!do_row && !do_col) return;  // uniform across the workgroup
 
   float v[16][8];
-  load_patch(static_cast<const TIn*>(a.x), tile_r0, min(rows - tile_r0, (int64_t)kTileR), cols,
+  load_patch(static_cast<const TIn*>(a.x), tile_r0, min(rows - tile_r0, (int64_t)TR), cols,
              a.ld, rs * 16, c0, v);
 
   if (TWO_D) {
@@ -335,9 +363,11 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
 
 template <typename TIn, int F>
 static void launch_tile(const TileArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.cols + kTileC - 1) / kTileC),
-                  (unsigned)((a.rows + kTileR - 1) / kTileR));
-  hipLaunchKernelGGL((quant_tile_kernel<TIn, F>), grid, dim3(kThreads), 0, s, a);
+  constexpr int TR = emit_rows(F);
+  const int64_t gx = (a.cols + kTileC - 1) / kTileC, gy = (a.rows + TR - 1) / TR;
+  const int64_t pairs = gx * ((gy + 1) / 2);
+  const dim3 grid((unsigned)(16 * ((pairs + 7) / 8)));
+  hipLaunchKernelGGL((quant_tile_kernel<TIn, F>), grid, dim3(2 * TR), 0, s, a);
 }
 
 template <typename TIn>

@@ -37,7 +37,8 @@
  *     share a workspace must be issued on one stream (they reuse its slots).
  *   - Shapes: rows and cols are multiples of 16 except where stated; leading
  *     dimensions are in elements and >= cols, with 256 * ld * element size
- *     below 2^31 bytes (rows are read in 256-row tiles with 32-bit offsets);
+ *     below 2^31 bytes (rows are read in 256-row tiles with 32-bit offsets)
+ *     and at most 65535 * 128 = 8388480 rows per source matrix;
  *     device pointers must be 16-byte aligned and ld * element size a
  *     multiple of 16 bytes; a GEMM operand's scales pointer must be 4-byte
  *     aligned.

@@ -73,6 +73,7 @@ def test_quantize_argument_errors():
     assert _q(cols=24, ld=24) == nv.ERR_SHAPE
     assert _q(rows=0) == nv.ERR_SHAPE
     assert _q(ld=128) == nv.ERR_SHAPE
+    assert _q(rows=65535 * 128 + 16, cols=16, ld=16) == nv.ERR_SHAPE   # row limit
     assert _q(x=P + 2) == nv.ERR_ALIGN
     assert _q(ld=260) == nv.ERR_ALIGN
     assert _q(out=_tensor(codes=P + 4)) == nv.ERR_ALIGN
@@ -152,6 +153,7 @@ def test_2d_rht_and_layer_argument_errors():
                                      None) == nv.ERR_SHAPE
     assert nv._lib.nvfp4_rht16(P, P, nv.F32, 24, 32, 32, 0, 0, None) == nv.ERR_SHAPE
     assert nv._lib.nvfp4_rht16(P, P, nv.F32, 32, 24, 24, 1, 0, None) == nv.ERR_SHAPE
+    assert nv._lib.nvfp4_rht16(P, P, nv.F32, 65535 * 128 + 16, 16, 16, 1, 0, None) == nv.ERR_SHAPE
     assert nv._lib.nvfp4_rht16(None, P, nv.F32, 32, 32, 32, 1, 0, None) == nv.ERR_NULL
     assert nv._lib.nvfp4_rht16(P, P, nv.F32, 32, 32, 32, 2, 0, None) == nv.ERR_DTYPE
     rec = nv.c_recipe(0, 1)
