@@ -253,26 +253,153 @@ __device__ __forceinline__ void zero_acc(float16_t (&acc)[4][NB]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
+// 4x4 transpose over the lanes of each quad: on entry lane t of a quad holds
+// x[k] = element (k, t) of a 4x4 block, on exit x[k] = element (t, k).  Two
+// DPP exchanges: with lane ^ 1 the elements whose index parity differs from
+// the lane's, then with lane ^ 2 those whose index bit 1 differs.
+__device__ __forceinline__ float quad_dpp(float v, int ctrl_xor) {
+  return __int_as_float(ctrl_xor == 1 ? __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)
+                                      : __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(float (&x)[4], int lane) {
+  const bool odd = lane & 1, up = lane & 2;
+  const float a0 = x[0], a1 = x[1], a2 = x[2], a3 = x[3];
+  const float r0 = quad_dpp(odd ? a0 : a1, 1), r1 = quad_dpp(odd ? a2 : a3, 1);
+  const float b0 = odd ? r0 : a0, b1 = odd ? a1 : r0, b2 = odd ? r1 : a2, b3 = odd ? a3 : r1;
+  const float u0 = quad_dpp(up ? b0 : b2, 2), u1 = quad_dpp(up ? b1 : b3, 2);
+  x[0] = up ? u0 : b0;
+  x[1] = up ? u1 : b1;
+  x[2] = up ? b2 : u0;
+  x[3] = up ? b3 : u1;
+}
+
 // Scaled accumulators -> C (bf16 nearest-even or fp32); rows and columns past
 // the operands are not stored.  (mw, nw) is the wave's first row and column.
+// A lane's accumulator holds one column of C at rows 4 apart in groups of 4
+// consecutive rows (lanes 32-63 four rows below lanes 0-31).
+//   fp32: each store writes one row's 32 columns (128 bytes) per half-wave.
+//   bf16: a quad transpose turns each group into 4 consecutive columns of one
+//   row (8 bytes), and a lane-half swap between column blocks j and j + 1
+//   puts block j + 1's lanes 0-31 beside block j's, so one store writes 64
+//   columns, a whole 128-byte line, of each of 4 rows; a store that covered
+//   only half lines took as long as the fp32 store of twice the bytes.  The
+//   8-byte stores need C's rows and base 8-byte aligned (`vec`); otherwise,
+//   and for the last columns, elements are stored one by one.  The rounding
+//   is gfx950's packed convert (nearest-even, denormals kept; it matches the
+//   software rounding on every non-NaN fp32 value).
 template <bool OUT_BF16, int NB>
 __device__ __forceinline__ void store_tile(const float16_t (&acc)[4][NB], float gab, int64_t mw,
                                            int64_t nw, int64_t rows_a, int64_t rows_b, int lane,
                                            void* __restrict__ c, int64_t ldc) {
+  constexpr int64_t kEs = OUT_BF16 ? 2 : 4;
+  const int t = lane & 3, q = (lane & 31) >> 2, h = lane >> 5;
+  // The common case -- the wave's 128 x 32NB block lies inside C, its rows
+  // are 8-byte aligned and 32-bit offsets reach all of it -- has no bounds
+  // checks: buffer stores from the block's corner, with the lane's offset
+  // fixed for the whole block and each store's row offset a scalar.
+  const bool full = mw + 128 <= rows_a && nw + 32 * NB <= rows_b && ldc * 128 * kEs < ((int64_t)1 << 31) &&
+                    (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(c) & 7) == 0;
+  if (full) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(c) + (mw * ldc + nw) * kEs, (short)0, (int)((127 * ldc + 32 * NB) * kEs),
+        0x00020000);
+    const int ld = (int)ldc;
+    if (!OUT_BF16) {
+      const int vo = (4 * h * ld + (lane & 31)) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r] * gab), rs, vo,
+                                                  ((i * 32 + 8 * (r >> 2) + (r & 3)) * ld + 32 * j) * 4, 0);
+    } else {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      const int vo = (t * ld + 32 * h + 4 * q) * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jp = 0; jp < NB / 2; ++jp)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint32_t lo[2], hi[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              float x[4];
+#pragma unroll
+              for (int k = 0; k < 4; ++k) x[k] = acc[i][2 * jp + e][4 * g + k] * gab;
+              quad_transpose(x, lane);
+              const bf16x2_t p0 = {(__bf16)x[0], (__bf16)x[1]}, p1 = {(__bf16)x[2], (__bf16)x[3]};
+              __builtin_memcpy(&lo[e], &p0, 4);
+              __builtin_memcpy(&hi[e], &p1, 4);
+            }
+            const auto sl = __builtin_amdgcn_permlane32_swap(lo[0], lo[1], false, false);
+            const auto sh = __builtin_amdgcn_permlane32_swap(hi[0], hi[1], false, false);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const u32x2_t w = {sl[e], sh[e]};
+              __builtin_amdgcn_raw_buffer_store_b64(w, rs, vo,
+                                                    ((i * 32 + 8 * g + 4 * e) * ld + 64 * jp) * 2, 0);
+            }
+          }
+    }
+    return;
+  }
+  if (!OUT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = mw + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int64_t n = nw + j * 32 + (lane & 31);
+          if (m < rows_a && n < rows_b) static_cast<float*>(c)[m * ldc + n] = acc[i][j][r] * gab;
+        }
+    return;
+  }
+  static_assert(NB % 2 == 0, "column blocks are stored in pairs");
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bool vec = (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(c) & 7) == 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int jp = 0; jp < NB / 2; ++jp)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = mw + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t n = nw + j * 32 + (lane & 31);
-        if (m < rows_a && n < rows_b) {
-          const float v = acc[i][j][r] * gab;
-          if (OUT_BF16)
-            static_cast<uint16_t*>(c)[m * ldc + n] = f32_to_bf16_rne(v);
-          else
-            static_cast<float*>(c)[m * ldc + n] = v;
+      for (int g = 0; g < 4; ++g) {
+        uint32_t lo[2], hi[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          float x[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[k] = acc[i][2 * jp + e][4 * g + k] * gab;
+          quad_transpose(x, lane);
+          const bf16x2_t p0 = {(__bf16)x[0], (__bf16)x[1]}, p1 = {(__bf16)x[2], (__bf16)x[3]};
+          __builtin_memcpy(&lo[e], &p0, 4);
+          __builtin_memcpy(&hi[e], &p1, 4);
+        }
+        // lanes 32-63 of block 2jp <-> lanes 0-31 of block 2jp+1: the first
+        // result holds rows +0..3, the second rows +4..7, of 64 columns
+        const auto sl = __builtin_amdgcn_permlane32_swap(lo[0], lo[1], false, false);
+        const auto sh = __builtin_amdgcn_permlane32_swap(hi[0], hi[1], false, false);
+        const int64_t n0 = nw + jp * 64 + 32 * h + 4 * q;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int64_t m = mw + i * 32 + 8 * g + 4 * e + t;
+          if (m >= rows_a) continue;
+          const uint2 w = make_uint2(sl[e], sh[e]);
+          uint16_t* row = static_cast<uint16_t*>(c) + m * ldc;
+          if (vec && n0 + 3 < rows_b) {
+            *reinterpret_cast<uint2*>(row + n0) = w;
+          } else {
+            const uint16_t v[4] = {(uint16_t)w.x, (uint16_t)(w.x >> 16), (uint16_t)w.y,
+                                   (uint16_t)(w.y >> 16)};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (n0 + k < rows_b) row[n0 + k] = v[k];
+          }
         }
       }
 }
