@@ -220,13 +220,4 @@ __device__ __forceinline__ void rht16_inplace(float* u, uint32_t signs) {
   for (int i = 0; i < 16; ++i) u[i * S] = u[i * S] * 0.25f;
 }
 
-// ---------------------------------------------------------------- bf16 out
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7FFFFFFFu) > kInfBits) return (uint16_t)((b >> 16) | 0x40u);  // quiet NaN
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
-}
-
 }  // namespace nvfp4

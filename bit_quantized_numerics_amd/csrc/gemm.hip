@@ -138,7 +138,7 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, uint32_t dpair, boo
 // sub-step 0 and mem2(G) in sub-step 1 (loads of later K-steps, one per chunk
 // so that no burst of them holds up the MFMA stream).  A scheduling fence
 // after each chunk keeps this order.
-template <int S, int NB, class Mem, class Mem2>
+template <int S, bool TR, int NB, class Mem, class Mem2>
 __device__ __forceinline__ void sub_step(float16_t (&acc)[4][NB], const FragsT<NB>& src,
                                          FragsT<NB>& dst, uint32_t (&dp)[4 + NB],
                                          const StepRawT<NB>& cur, const StepRawT<NB>& nxt,
@@ -148,8 +148,10 @@ __device__ __forceinline__ void sub_step(float16_t (&acc)[4][NB], const FragsT<N
 #pragma unroll
   for (int G = 0; G < 4 * NB; ++G) {
     const int i = G / NB, j = G % NB;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(src.w[i]), as_half8(src.w[4 + j]),
-                                                       acc[i][j], 0, 0, 0);
+    acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(src.w[4 + j]),
+                                                            as_half8(src.w[i]), acc[i][j], 0, 0, 0)
+                   : __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(src.w[i]),
+                                                            as_half8(src.w[4 + j]), acc[i][j], 0, 0, 0);
     if (S == 0) mem(G);
     if (S == 1) mem2(G);
 #pragma unroll
@@ -174,16 +176,16 @@ struct NoMem {
 // One K-step of 64: on entry `f` holds sub-step 0 of `cur` and dp its scales;
 // on exit they hold sub-step 0 of `nxt`.  mem(G) runs during sub-step 0,
 // mem2(G) during sub-step 1.
-template <int NB, class Mem, class Mem2 = NoMem>
+template <bool TR, int NB, class Mem, class Mem2 = NoMem>
 __device__ __forceinline__ void k_step(float16_t (&acc)[4][NB], FragsT<NB>& f,
                                        uint32_t (&dp)[4 + NB], const StepRawT<NB>& cur,
                                        const StepRawT<NB>& nxt, bool nxt_in_k, uint32_t sel,
                                        Mem& mem, Mem2 mem2 = Mem2()) {
   FragsT<NB> g;
-  sub_step<0>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
-  sub_step<1>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
-  sub_step<2>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
-  sub_step<3>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
+  sub_step<0, TR>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
+  sub_step<1, TR>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
+  sub_step<2, TR>(acc, f, g, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
+  sub_step<3, TR>(acc, g, f, dp, cur, nxt, nxt_in_k, sel, mem, mem2);
 }
 
 // Sub-step 0 fragments and scales of the first K-step.
@@ -253,152 +255,137 @@ __device__ __forceinline__ void zero_acc(float16_t (&acc)[4][NB]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
-// 4x4 transpose over the lanes of each quad: on entry lane t of a quad holds
-// x[k] = element (k, t) of a 4x4 block, on exit x[k] = element (t, k).  Two
-// DPP exchanges: with lane ^ 1 the elements whose index parity differs from
-// the lane's, then with lane ^ 2 those whose index bit 1 differs.
-__device__ __forceinline__ float quad_dpp(float v, int ctrl_xor) {
-  return __int_as_float(ctrl_xor == 1 ? __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)
-                                      : __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-__device__ __forceinline__ void quad_transpose(float (&x)[4], int lane) {
-  const bool odd = lane & 1, up = lane & 2;
-  const float a0 = x[0], a1 = x[1], a2 = x[2], a3 = x[3];
-  const float r0 = quad_dpp(odd ? a0 : a1, 1), r1 = quad_dpp(odd ? a2 : a3, 1);
-  const float b0 = odd ? r0 : a0, b1 = odd ? a1 : r0, b2 = odd ? r1 : a2, b3 = odd ? a3 : r1;
-  const float u0 = quad_dpp(up ? b0 : b2, 2), u1 = quad_dpp(up ? b1 : b3, 2);
-  x[0] = up ? u0 : b0;
-  x[1] = up ? u1 : b1;
-  x[2] = up ? b2 : u0;
-  x[3] = up ? b3 : u1;
-}
-
 // Scaled accumulators -> C (bf16 nearest-even or fp32); rows and columns past
 // the operands are not stored.  (mw, nw) is the wave's first row and column.
-// A lane's accumulator holds one column of C at rows 4 apart in groups of 4
-// consecutive rows (lanes 32-63 four rows below lanes 0-31).
-//   fp32: each store writes one row's 32 columns (128 bytes) per half-wave.
-//   bf16: a quad transpose turns each group into 4 consecutive columns of one
-//   row (8 bytes), and a lane-half swap between column blocks j and j + 1
-//   puts block j + 1's lanes 0-31 beside block j's, so one store writes 64
-//   columns, a whole 128-byte line, of each of 4 rows; a store that covered
-//   only half lines took as long as the fp32 store of twice the bytes.  The
-//   8-byte stores need C's rows and base 8-byte aligned (`vec`); otherwise,
-//   and for the last columns, elements are stored one by one.  The rounding
-//   is gfx950's packed convert (nearest-even, denormals kept; it matches the
-//   software rounding on every non-NaN fp32 value).
-template <bool OUT_BF16, int NB>
+// With TR (kernels whose first output is bf16) every MFMA takes the B block
+// as its first operand, so accumulator (i, j) is the transposed 32 x 32
+// block: lane l holds row 32 i + l % 32 of the wave's rows and, in register
+// 4 g + k, column 32 j + 8 g + 4 (l / 32) + k.  Without TR (fp32-only
+// kernels) the layout is the natural one, described below, whose 4-byte
+// stores each write a 128-byte row segment per half-wave and measured faster
+// for fp32 than the transposed layout's 16-byte stores over 32 rows.
+// Each lane's 4 registers of a group are thus 4 consecutive columns of one
+// row: fp32 stores them as one 16-byte write; bf16 packs them into 8 bytes
+// and a lane-half swap between groups 2p and 2p + 1 gives every lane 8
+// consecutive columns (16 bytes).  The bf16 rounding is gfx950's packed
+// convert (nearest-even, denormals kept; it matches the software rounding on
+// every non-NaN fp32 value).
+//
+// The common case -- the wave's 128 x 32 NB block inside C, rows and base
+// 16-byte aligned, 32-bit offsets reaching all of it -- has no bounds checks:
+// buffer stores from the block's corner with a per-lane offset fixed for the
+// whole block and each store's remaining offset a scalar.  Other blocks store
+// element by element with checks.
+template <bool OUT_BF16, bool TR, int NB>
 __device__ __forceinline__ void store_tile(const float16_t (&acc)[4][NB], float gab, int64_t mw,
                                            int64_t nw, int64_t rows_a, int64_t rows_b, int lane,
                                            void* __restrict__ c, int64_t ldc) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   constexpr int64_t kEs = OUT_BF16 ? 2 : 4;
-  const int t = lane & 3, q = (lane & 31) >> 2, h = lane >> 5;
-  // The common case -- the wave's 128 x 32NB block lies inside C, its rows
-  // are 8-byte aligned and 32-bit offsets reach all of it -- has no bounds
-  // checks: buffer stores from the block's corner, with the lane's offset
-  // fixed for the whole block and each store's row offset a scalar.
-  const bool full = mw + 128 <= rows_a && nw + 32 * NB <= rows_b && ldc * 128 * kEs < ((int64_t)1 << 31) &&
-                    (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(c) & 7) == 0;
-  if (full) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<char*>(c) + (mw * ldc + nw) * kEs, (short)0, (int)((127 * ldc + 32 * NB) * kEs),
-        0x00020000);
-    const int ld = (int)ldc;
-    if (!OUT_BF16) {
-      const int vo = (4 * h * ld + (lane & 31)) * 4;
+  const int rl = lane & 31, h = lane >> 5;
+  if (!TR) {
+    static_assert(TR || !OUT_BF16, "bf16 output uses the transposed layout");
+    // natural layout: lane l holds column l % 32 and, in register r, row
+    // 8 (r / 4) + 4 (l / 32) + r % 4; each store writes 128 bytes of one row
+    // per half-wave
+    const bool full_n = mw + 128 <= rows_a && nw + 32 * NB <= rows_b &&
+                        ldc * 128 * kEs < ((int64_t)1 << 31);
+    if (full_n) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<char*>(c) + (mw * ldc + nw) * kEs, (short)0,
+          (int)((127 * ldc + 32 * NB) * kEs), 0x00020000);
+      const int ld = (int)ldc, vo = (4 * h * ld + rl) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r] * gab), rs, vo,
-                                                  ((i * 32 + 8 * (r >> 2) + (r & 3)) * ld + 32 * j) * 4, 0);
-    } else {
-      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-      const int vo = (t * ld + 32 * h + 4 * q) * 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jp = 0; jp < NB / 2; ++jp)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            uint32_t lo[2], hi[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              float x[4];
-#pragma unroll
-              for (int k = 0; k < 4; ++k) x[k] = acc[i][2 * jp + e][4 * g + k] * gab;
-              quad_transpose(x, lane);
-              const bf16x2_t p0 = {(__bf16)x[0], (__bf16)x[1]}, p1 = {(__bf16)x[2], (__bf16)x[3]};
-              __builtin_memcpy(&lo[e], &p0, 4);
-              __builtin_memcpy(&hi[e], &p1, 4);
-            }
-            const auto sl = __builtin_amdgcn_permlane32_swap(lo[0], lo[1], false, false);
-            const auto sh = __builtin_amdgcn_permlane32_swap(hi[0], hi[1], false, false);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const u32x2_t w = {sl[e], sh[e]};
-              __builtin_amdgcn_raw_buffer_store_b64(w, rs, vo,
-                                                    ((i * 32 + 8 * g + 4 * e) * ld + 64 * jp) * 2, 0);
-            }
-          }
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(acc[i][j][r] * gab), rs, vo,
+                ((i * 32 + 8 * (r >> 2) + (r & 3)) * ld + 32 * j) * 4, 0);
+      return;
     }
-    return;
-  }
-  if (!OUT_BF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t m = mw + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int64_t n = nw + j * 32 + (lane & 31);
+          const int64_t m = mw + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int64_t n = nw + j * 32 + rl;
           if (m < rows_a && n < rows_b) static_cast<float*>(c)[m * ldc + n] = acc[i][j][r] * gab;
         }
     return;
   }
-  static_assert(NB % 2 == 0, "column blocks are stored in pairs");
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bool vec = (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(c) & 7) == 0;
+  const bool full = mw + 128 <= rows_a && nw + 32 * NB <= rows_b &&
+                    ldc * 128 * kEs < ((int64_t)1 << 31) && (ldc * kEs) % 16 == 0 &&
+                    (reinterpret_cast<uintptr_t>(c) & 15) == 0;
+  if (full) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(c) + (mw * ldc + nw) * kEs, (short)0, (int)((127 * ldc + 32 * NB) * kEs),
+        0x00020000);
+    const int ld = (int)ldc;
+    if (!OUT_BF16) {
+      const int vo = (rl * ld + 4 * h) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const u32x4_t w = {__float_as_uint(acc[i][j][4 * g] * gab),
+                               __float_as_uint(acc[i][j][4 * g + 1] * gab),
+                               __float_as_uint(acc[i][j][4 * g + 2] * gab),
+                               __float_as_uint(acc[i][j][4 * g + 3] * gab)};
+            __builtin_amdgcn_raw_buffer_store_b128(w, rs, vo, (32 * i * ld + 32 * j + 8 * g) * 4, 0);
+          }
+    } else {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const int vo = (rl * ld + 8 * h) * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            uint32_t lo[2], hi[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int g = 2 * p + e;
+              const bf16x2_t p0 = {(__bf16)(acc[i][j][4 * g] * gab), (__bf16)(acc[i][j][4 * g + 1] * gab)};
+              const bf16x2_t p1 = {(__bf16)(acc[i][j][4 * g + 2] * gab),
+                                   (__bf16)(acc[i][j][4 * g + 3] * gab)};
+              __builtin_memcpy(&lo[e], &p0, 4);
+              __builtin_memcpy(&hi[e], &p1, 4);
+            }
+            // lanes 32-63 of group 2p <-> lanes 0-31 of group 2p+1: lanes
+            // 0-31 then hold columns 16p .. 16p+7, lanes 32-63 16p+8 .. 16p+15
+            const auto sl = __builtin_amdgcn_permlane32_swap(lo[0], lo[1], false, false);
+            const auto sh = __builtin_amdgcn_permlane32_swap(hi[0], hi[1], false, false);
+            const u32x4_t w = {sl[0], sh[0], sl[1], sh[1]};
+            __builtin_amdgcn_raw_buffer_store_b128(w, rs, vo, (32 * i * ld + 32 * j + 16 * p) * 2, 0);
+          }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int jp = 0; jp < NB / 2; ++jp)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint32_t lo[2], hi[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          float x[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) x[k] = acc[i][2 * jp + e][4 * g + k] * gab;
-          quad_transpose(x, lane);
-          const bf16x2_t p0 = {(__bf16)x[0], (__bf16)x[1]}, p1 = {(__bf16)x[2], (__bf16)x[3]};
-          __builtin_memcpy(&lo[e], &p0, 4);
-          __builtin_memcpy(&hi[e], &p1, 4);
-        }
-        // lanes 32-63 of block 2jp <-> lanes 0-31 of block 2jp+1: the first
-        // result holds rows +0..3, the second rows +4..7, of 64 columns
-        const auto sl = __builtin_amdgcn_permlane32_swap(lo[0], lo[1], false, false);
-        const auto sh = __builtin_amdgcn_permlane32_swap(hi[0], hi[1], false, false);
-        const int64_t n0 = nw + jp * 64 + 32 * h + 4 * q;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int64_t m = mw + i * 32 + 8 * g + 4 * e + t;
-          if (m >= rows_a) continue;
-          const uint2 w = make_uint2(sl[e], sh[e]);
-          uint16_t* row = static_cast<uint16_t*>(c) + m * ldc;
-          if (vec && n0 + 3 < rows_b) {
-            *reinterpret_cast<uint2*>(row + n0) = w;
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = mw + i * 32 + rl;
+        const int64_t n = nw + j * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < rows_a && n < rows_b) {
+          const float v = acc[i][j][r] * gab;
+          if (OUT_BF16) {
+            const __bf16 b = (__bf16)v;
+            uint16_t u;
+            __builtin_memcpy(&u, &b, 2);
+            static_cast<uint16_t*>(c)[m * ldc + n] = u;
           } else {
-            const uint16_t v[4] = {(uint16_t)w.x, (uint16_t)(w.x >> 16), (uint16_t)w.y,
-                                   (uint16_t)(w.y >> 16)};
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              if (n0 + k < rows_b) row[n0 + k] = v[k];
+            static_cast<float*>(c)[m * ldc + n] = v;
           }
         }
       }
@@ -472,6 +459,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_direct_kernel(GemmOperan
                                                                       void* __restrict__ c,
                                                                       int64_t ldc, int tiles_m,
                                                                       int tiles_n) {
+  constexpr bool TR = OUT_BF16;  // accumulator layout (store_tile)
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
@@ -503,15 +491,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_direct_kernel(GemmOperan
   first_frags(r0, sel, f, dp);
   for (int64_t kt = 0; kt < nk; kt += 3) {
     DirectMem l2{oa, ob, K, (kt + 2) * kBK, h, r2};
-    k_step(acc, f, dp, r0, r1, (kt + 1) * kBK < K, sel, l2);
+    k_step<TR>(acc, f, dp, r0, r1, (kt + 1) * kBK < K, sel, l2);
     DirectMem l0{oa, ob, K, (kt + 3) * kBK, h, r0};
-    k_step(acc, f, dp, r1, r2, (kt + 2) * kBK < K, sel, l0);
+    k_step<TR>(acc, f, dp, r1, r2, (kt + 2) * kBK < K, sel, l0);
     DirectMem l1{oa, ob, K, (kt + 4) * kBK, h, r1};
-    k_step(acc, f, dp, r2, r0, (kt + 3) * kBK < K, sel, l1);
+    k_step<TR>(acc, f, dp, r2, r0, (kt + 3) * kBK < K, sel, l1);
   }
 
   const float gab = (*a.global) * (*b.global) * 65536.0f;
-  store_tile<OUT_BF16>(acc, gab, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, c, ldc);
+  store_tile<OUT_BF16, TR>(acc, gab, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, c, ldc);
 }
 
 // ------------------------------------------------------------ slab kernel
@@ -668,7 +656,7 @@ struct SlabMem {
 // reads any more) and the last K-step reads a buffer it does not use, which
 // keeps every wait count and the loop free of branches: a branch here would
 // make the compiler move the accumulators out of AGPRs.
-template <int NW, int NB>
+template <bool TR, int NW, int NB>
 __device__ __forceinline__ void slab_step(float16_t (&acc)[4][NB], FragsT<NB>& f,
                                           uint32_t (&dp)[4 + NB], StepRawT<NB>& r0,
                                           StepRawT<NB>& r1, const uint8_t* lds,
@@ -676,12 +664,12 @@ __device__ __forceinline__ void slab_step(float16_t (&acc)[4][NB], FragsT<NB>& f
                                           int ns, uint32_t sel) {
   const int u = s & 3;
   SlabMem<1, NB> m1{lds, R, u, r1};
-  k_step(acc, f, dp, r0, r1, true, sel, m1);
+  k_step<TR>(acc, f, dp, r0, r1, true, sel, m1);
   wait_vmcnt<slab_loads(NW)>();  // this wave's loads of slab s+1 landed (s+2 may be in flight)
   __builtin_amdgcn_s_barrier();  // ... and every wave's; slab s-1's buffer is free
   SlabMem<0, NB> m0{lds, R, (u + 1) & 3, r0};
-  k_step(acc, f, dp, r1, r0, true, sel, m0,
-         SlabDma<NW>{L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3});
+  k_step<TR>(acc, f, dp, r1, r0, true, sel, m0,
+             SlabDma<NW>{L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3});
 }
 
 // One GEMM of a slab-kernel launch.
@@ -699,6 +687,7 @@ struct GemmProblem {
 // row blocks of 32 columns each).
 template <bool OUT0_BF16, bool OUT1_BF16, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_lds_kernel(GemmProblem p0, GemmProblem p1) {
+  constexpr bool TR = OUT0_BF16;  // accumulator layout (store_tile)
   constexpr int WN = NW / 2, NB = 8 / WN;  // waves along N, B row blocks per wave
   constexpr int SG = SlabLoader<NW>::SG, CG = SlabLoader<NW>::CG;
   __shared__ __align__(16) uint8_t lds[kLdsBytes];
@@ -785,14 +774,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_lds_kernel(GemmProblem p0, Ge
   FragsT<NB> f;
   uint32_t dp[4 + NB];
   first_frags(r0, sel, f, dp);
-  for (int s = 0; s < ns; ++s) slab_step(acc, f, dp, r0, r1, lds, R, L, s, ns, sel);
+  for (int s = 0; s < ns; ++s) slab_step<TR>(acc, f, dp, r0, r1, lds, R, L, s, ns, sel);
   wait_vmcnt<0>();  // no LDS-mode load may outlive the workgroup's LDS
 
   const float gab = (*a.global) * (*b.global) * 65536.0f;
   if (OUT0_BF16 == OUT1_BF16 || prob == 0)
-    store_tile<OUT0_BF16>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
+    store_tile<OUT0_BF16, TR>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
   else
-    store_tile<OUT1_BF16>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
+    store_tile<OUT1_BF16, TR>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
 }
 
 // ------------------------------------------------------------ 128-byte-row NVFP4 slabs
@@ -887,6 +876,7 @@ struct XSlabMem {
 
 template <bool OUT0_BF16, bool OUT1_BF16>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmProblem p0, GemmProblem p1) {
+  constexpr bool TR = OUT0_BF16;  // accumulator layout (store_tile)
   constexpr int NB = 4;
   __shared__ __align__(16) uint8_t lds[kLdsBytes];
   const int t = threadIdx.x, lane = t & 63;
@@ -973,30 +963,30 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmProblem p0, GemmP
     const int u = s & 1;
     {
       XSlabMem<1> m{lds, R, u, r1};
-      k_step(acc, f, dp, r0, r1, true, sel, m);
+      k_step<TR>(acc, f, dp, r0, r1, true, sel, m);
     }
     {
       XSlabMem<2> m{lds, R, u, r0};
-      k_step(acc, f, dp, r1, r0, true, sel, m);
+      k_step<TR>(acc, f, dp, r1, r0, true, sel, m);
     }
     {
       XSlabMem<3> m{lds, R, u, r1};
-      k_step(acc, f, dp, r0, r1, true, sel, m);
+      k_step<TR>(acc, f, dp, r0, r1, true, sel, m);
     }
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): slab s+1, reads of slab s
     __builtin_amdgcn_s_barrier();        // ... in every wave: buffer u is free
     {
       XSlabMem<0> m{lds, R, u ^ 1, r0};
-      k_step(acc, f, dp, r1, r0, true, sel, m, XSlabDma{L, s + 2 < ns ? s + 2 : 0, u});
+      k_step<TR>(acc, f, dp, r1, r0, true, sel, m, XSlabDma{L, s + 2 < ns ? s + 2 : 0, u});
     }
   }
   wait_vmcnt<0>();  // no LDS-mode load may outlive the workgroup's LDS
 
   const float gab = (*a.global) * (*b.global) * 65536.0f;
   if (OUT0_BF16 == OUT1_BF16 || prob == 0)
-    store_tile<OUT0_BF16>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
+    store_tile<OUT0_BF16, TR>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
   else
-    store_tile<OUT1_BF16>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
+    store_tile<OUT1_BF16, TR>(acc, gab, m0 + wm * 128, n0 + brow0, a.rows, b.rows, lane, P.c, P.ldc);
 }
 
 // ------------------------------------------------------------ MXFP4 / BF16 kernel
@@ -1099,7 +1089,7 @@ __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
 // One K-step: 16 MFMAs on `cur`, in issue order; chunk G also runs mem(G)
 // and mem2(G).  MXFP4: 64 k per scaled FP4 MFMA with the slab's scale
 // groups (byte 2 J + h of each row block's dword).  BF16: 16 k per MFMA.
-template <int FMT, int J, class Mem, class Mem2>
+template <int FMT, int J, bool TR, class Mem, class Mem2>
 __device__ __forceinline__ void mx_kstep(float16_t (&acc)[4][4], const MxRaw& cur, const uint4& sa,
                                          const uint4& sb, int h, Mem& mem, Mem2& mem2) {
   typedef int v8i __attribute__((ext_vector_type(8)));
@@ -1112,13 +1102,18 @@ __device__ __forceinline__ void mx_kstep(float16_t (&acc)[4][4], const MxRaw& cu
     if (FMT == kFmtMx) {
       const v8i A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
       const v8i B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          A, B, acc[i][j], 4, 4, 0, (int)(u4_get(sa, i) >> sh), 0, (int)(u4_get(sb, j) >> sh));
+      acc[i][j] = TR ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                           B, A, acc[i][j], 4, 4, 0, (int)(u4_get(sb, j) >> sh), 0,
+                           (int)(u4_get(sa, i) >> sh))
+                     : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                           A, B, acc[i][j], 4, 4, 0, (int)(u4_get(sa, i) >> sh), 0,
+                           (int)(u4_get(sb, j) >> sh));
     } else {
       bf16x8_t A, B;
       __builtin_memcpy(&A, &a, 16);
       __builtin_memcpy(&B, &b, 16);
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[i][j], 0, 0, 0);
+      acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(B, A, acc[i][j], 0, 0, 0)
+                     : __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[i][j], 0, 0, 0);
     }
     mem(G);
     mem2(G);
@@ -1128,6 +1123,7 @@ __device__ __forceinline__ void mx_kstep(float16_t (&acc)[4][4], const MxRaw& cu
 
 template <bool OUT_BF16, int FMT>
 __global__ __launch_bounds__(kGemmThreads, 1) void mxfp4_gemm_kernel(GemmProblem P) {
+  constexpr bool TR = OUT_BF16;  // accumulator layout (store_tile)
   constexpr bool MX = FMT == kFmtMx;
   constexpr int kSlabElems = MX ? kSlabK : 32;   // k per slab (64 bytes per row)
   constexpr int kLoads = MX ? kMxSlabLoads : 8;   // BF16: code loads only
@@ -1193,18 +1189,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxfp4_gemm_kernel(GemmProblem
     const int u = s & 3;
     MxMem<1, false> m1{lds, rca[1], rcb[1], rsa, rsb, u, r1, sa_n, sb_n};
     NoMem none;
-    mx_kstep<FMT, 0>(acc, r0, sa, sb, h, m1, none);
+    mx_kstep<FMT, 0, TR>(acc, r0, sa, sb, h, m1, none);
     wait_vmcnt<kLoads>();
     __builtin_amdgcn_s_barrier();
     MxMem<0, MX> m0{lds, rca[0], rcb[0], rsa, rsb, (u + 1) & 3, r0, sa_n, sb_n};
     MxDma dma{L, s + 3 < ns ? s + 3 : 0, (u + 3) & 3, kLoads};
-    mx_kstep<FMT, 1>(acc, r1, sa, sb, h, m0, dma);
+    mx_kstep<FMT, 1, TR>(acc, r1, sa, sb, h, m0, dma);
     sa = sa_n;
     sb = sb_n;
   }
   wait_vmcnt<0>();
 
-  store_tile<OUT_BF16>(acc, 1.0f, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, P.c, P.ldc);
+  store_tile<OUT_BF16, TR>(acc, 1.0f, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, P.c, P.ldc);
 }
 
 // ------------------------------------------------------------ 128-byte-row slabs
@@ -1299,6 +1295,7 @@ struct WideMem {
 
 template <bool OUT_BF16, int FMT>
 __global__ __launch_bounds__(kGemmThreads, 1) void wide_gemm_kernel(GemmProblem P) {
+  constexpr bool TR = OUT_BF16;  // accumulator layout (store_tile)
   constexpr bool MX = FMT == kFmtMx;
   constexpr int kSlabElems = MX ? 256 : 64;      // k per slab (128 bytes per row)
   constexpr int kLoads = MX ? 20 : 16;
@@ -1369,15 +1366,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void wide_gemm_kernel(GemmProblem 
     NoMem none;
     {
       WideMem<MX ? 1 : -1> m{lds, rca[1], rcb[1], rsa, rsb, u, r1, sa1, sb1};
-      mx_kstep<FMT, 0>(acc, r0, sa0, sb0, h, m, none);
+      mx_kstep<FMT, 0, TR>(acc, r0, sa0, sb0, h, m, none);
     }
     {
       WideMem<-1> m{lds, rca[2], rcb[2], rsa, rsb, u, r0, sa1, sb1};
-      mx_kstep<FMT, 1>(acc, r1, sa0, sb0, h, m, none);
+      mx_kstep<FMT, 1, TR>(acc, r1, sa0, sb0, h, m, none);
     }
     {
       WideMem<-1> m{lds, rca[3], rcb[3], rsa, rsb, u, r1, sa1, sb1};
-      mx_kstep<FMT, 0>(acc, r0, sa1, sb1, h, m, none);
+      mx_kstep<FMT, 0, TR>(acc, r0, sa1, sb1, h, m, none);
     }
     // slab s+1 landed for this wave and its reads of buffer u are done; then
     // for every wave
@@ -1389,12 +1386,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void wide_gemm_kernel(GemmProblem 
       // sa1/sb1 still hold slab s's dword 1 for this K-step; sa0/sb0 are
       // overwritten with slab s+1's dword 0 by the reads (chunks 8, 9)
       const uint4 ka = sa1, kb = sb1;
-      mx_kstep<FMT, 1>(acc, r1, ka, kb, h, m, dma);
+      mx_kstep<FMT, 1, TR>(acc, r1, ka, kb, h, m, dma);
     }
   }
   wait_vmcnt<0>();
 
-  store_tile<OUT_BF16>(acc, 1.0f, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, P.c, P.ldc);
+  store_tile<OUT_BF16, TR>(acc, 1.0f, m0 + wm * 128, n0 + wn * 128, a.rows, b.rows, lane, P.c, P.ldc);
 }
 
 // ------------------------------------------------------------ launch
