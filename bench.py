@@ -42,10 +42,10 @@ BYTES_2D = 2.0 + 2 * (0.5 + 1.0 / 256)
 # HBM traffic of the GEMM kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (KiB per dispatch; FETCH_SIZE x 2 and WRITE_SIZE x 1, the factors a plain
 # 1 GiB device copy reads back), averaged over the single Fprop, Dgrad and
-# Wgrad launches: 1072.7, 875.8 and 1286.5 MB.  Valid only for the kernel
+# Wgrad launches: 1066.3, 874.1 and 1287.9 MB.  Valid only for the kernel
 # source it was measured on (profiles/hbm_traffic_gemm_quantize_*.md).
-GEMM_TRAFFIC = {"source_sha1": "2d422a70b368d9fc27e77ae03c4a4b897507db9b",
-                "bytes_per_launch": 1078.1e6}
+GEMM_TRAFFIC = {"source_sha1": "28e5980b0c25acaaf0736c43740a8233a60b1a35",
+                "bytes_per_launch": 1076.1e6}
 
 
 def _gemm_source_sha1() -> str:
