@@ -226,6 +226,38 @@ def bf16_fprop(nv, x, w, ctx, ws, signs, reps: int):
             "layer_fwd_bf16_fprop_ms": round(tf, 4), "layer_fwd_nvfp4_ms": round(tn, 4)}
 
 
+def layer_at(nv, W, m: int, signs: int, reps: int):
+    """The whole layer step (all quantisations and the three GEMMs, one stream)
+    at m tokens: X [m, K], W [N, K], dY [m, N] from the same generators."""
+    import torch
+    dev = "cuda:0"
+    x = W.activations(m, K).to(dev)
+    w = W.weights(N, K).to(dev)
+    dy = W.gradients(m, N).to(dev)
+    ws = nv.Workspace(dev)
+    nv.nvfp4_workspace_init(ws)
+    ctx = nv.LinearContext(m, K, N, dev)
+    y = torch.empty(m, N, dtype=torch.bfloat16, device=dev)
+    dx = torch.empty(m, K, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(N, K, dtype=torch.float32, device=dev)
+
+    def step():
+        nv.nvfp4_linear_fwd(x, w, ctx, ws, signs, training=True, y=y)
+        nv.nvfp4_linear_bwd(dy, ctx, ws, signs, W.SR_SEED, dx=dx, dw=dw)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / reps * 1e3
+    assert nv.nvfp4_device_status(ws) == nv.OK
+    return {"workload": f"NVFP4 linear layer fwd+bwd, {m} tokens, {K}->{N}", "steps": reps,
+            "ms_per_step": round(ms, 4), "TFLOPs": round(3 * 2.0 * m * N * K / (ms * 1e-3) / 1e12, 1)}
+
+
 def main():
     args = parse()
     if args.copy_mib:
@@ -334,14 +366,19 @@ def main():
     # memory traffic), next to the datasheet peak used in `roofline`
     nv.nvfp4_peak_mfma_f16(1000)
     mfma_loop = nv.nvfp4_peak_mfma_f16(5000)
+    mfma_5bit = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0x87C087C0)
     mfma_const = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0)
     out["measured_ceiling"] = {
         "mfma_f16_loop_TFLOPs": round(mfma_loop, 1),
+        "mfma_f16_loop_5bit_operands_TFLOPs": round(mfma_5bit, 1),
         "mfma_f16_loop_constant_operands_TFLOPs": round(mfma_const, 1),
         "gemm_frac_of_loop": round(achieved / mfma_loop, 4),
+        "gemm_frac_of_5bit_loop": round(achieved / mfma_5bit, 4),
         "note": "fp16 MFMA-only loop shaped like the GEMM's (16 accumulators per wave, 4 VALU per "
-                "MFMA), random-looking operands changing every iteration; and the same "
-                "instructions on constant operands"}
+                "MFMA): operands changing every iteration in sign, one exponent bit and all "
+                "mantissa bits; in sign, that exponent bit and the top 4 mantissa bits (the bit "
+                "pattern of dequantised E2M1 x E4M3 values); and constant operands"}
+    out["layer_16384_tokens"] = layer_at(nv, W, 2 * M, signs, max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
