@@ -298,8 +298,10 @@ nvfp4_status nvfp4_rht16(const void* x, float* y, int32_t in_dtype, int64_t rows
  * nvfp4_gemm: C[m][n] = g_a g_b sum_k (e2m1*d_b)_A[m][k] (e2m1*d_b)_B[n][k]
  * with FP32 accumulation [Review s6 step 1; Captions Fig. 5].  Both operands
  * are contiguous along k (a->cols == b->cols == K); either may use 1x16 or
- * 16x16 scales.  c: [M, N] row-major with leading dim ldc, dtype NVFP4_F32 or
- * NVFP4_BF16.  M, N multiples of 16; K a multiple of 16.
+ * 16x16 scales.  c: [M, N] row-major with leading dim ldc >= N, 4-byte aligned,
+ * dtype NVFP4_F32 or NVFP4_BF16 (nearest-even).  M and N may be any positive
+ * size (a 16x16-scaled operand needs rows % 16 == 0); K a multiple of 16.
+ * Only C's [M, N] window is written.
  * With both operands in NVFP4_SCALE_MX32 mode it is the MXFP4 product
  * C = sum_k (e2m1 * 2^(s-127))_A (e2m1 * 2^(s-127))_B (no tensor scales), on
  * gfx950's scaled FP4 MFMA; that path needs K % 128 == 0, K >= 384 and
