@@ -44,7 +44,7 @@ BYTES_2D = 2.0 + 2 * (0.5 + 1.0 / 256)
 # 1 GiB device copy reads back), averaged over the single Fprop, Dgrad and
 # Wgrad launches: 1066.3, 874.1 and 1287.9 MB.  Valid only for the kernel
 # source it was measured on (profiles/hbm_traffic_gemm_quantize_*.md).
-GEMM_TRAFFIC = {"source_sha1": "28e5980b0c25acaaf0736c43740a8233a60b1a35",
+GEMM_TRAFFIC = {"source_sha1": "79eb56f995e70372b7d5c4e1eca99b892bfd0083",
                 "bytes_per_launch": 1076.1e6}
 
 

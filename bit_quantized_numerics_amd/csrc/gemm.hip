@@ -25,9 +25,13 @@
 // row block of the next sub-step (4 VALU instructions: two converts, two
 // scale multiplies), written in issue order with a scheduling fence after
 // every MFMA so that the VALU work and the loads sit evenly in the MFMA
-// shadow.  Two kernels share that inner loop and differ in how the NVFP4
+// shadow.  Three kernels share that inner loop and differ in how the NVFP4
 // codes reach the registers:
 //
+//  * gemm_wide_kernel (K % 256 == 0: every layer shape): as gemm_lds_kernel
+//    below with 256-wide K slabs (128-byte row segments, which LDS-mode loads
+//    stream twice as fast as 64-byte ones), two buffers and one barrier per
+//    slab; described with its code further down.
 //  * gemm_lds_kernel (K % 128 == 0, K >= 384; the training shapes): the codes
 //    and scales of a 128-wide K slab of both 256-row operand tiles are copied
 //    straight from global memory into LDS by buffer loads in LDS mode (no VGPR
@@ -41,6 +45,11 @@
 //    codes straight from global memory into registers, two K-steps ahead,
 //    with the two waves that share rows meeting in L1.  Each load instruction
 //    touches one line per row, so this is the fallback for other shapes.
+//
+// Epilogue.  Kernels whose first output is bf16 pass the B block as each
+// MFMA's first operand, so a lane's accumulators hold 4 consecutive columns
+// of one C row and store_tile writes them without a transpose; fp32-only
+// kernels keep the natural layout (see store_tile).
 //
 // K order inside a step.  A K-step covers 64 k.  For MFMA sub-step s (0..3)
 // lane-half h (lanes 32h..32h+31) supplies k = 32h + 8s + (0..7) instead of
