@@ -179,6 +179,14 @@ void ctx_shapes(int64_t M, int64_t K, int64_t N, int64_t (&rc)[6][2]) {
 }
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// a * b for positive a, b, or false when it would pass 2^62 (sizes beyond any
+// device; keeps every size sum below in range).
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a > ((int64_t)1 << 62) / b) return false;
+  *out = a * b;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,6 +195,8 @@ nvfp4_status nvfp4_tensor_bytes(int64_t rows, int64_t cols, int32_t scale_mode, 
                                 size_t* scales_bytes) {
   if (!codes_bytes || !scales_bytes) return NVFP4_ERR_NULL;
   if (rows <= 0 || cols <= 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  int64_t codes = 0;
+  if (!mul_ok(rows, cols / 2, &codes)) return NVFP4_ERR_SHAPE;
   if (scale_mode == NVFP4_SCALE_MX32) {
     if (cols % 32 != 0) return NVFP4_ERR_SHAPE;
     *scales_bytes = (size_t)(rows * (cols / 32));
@@ -198,7 +208,7 @@ nvfp4_status nvfp4_tensor_bytes(int64_t rows, int64_t cols, int32_t scale_mode, 
   } else {
     return NVFP4_ERR_DTYPE;
   }
-  *codes_bytes = (size_t)(rows * (cols / 2));
+  *codes_bytes = (size_t)codes;
   return NVFP4_OK;
 }
 
@@ -209,6 +219,10 @@ nvfp4_status nvfp4_linear_ctx_bytes(int64_t M, int64_t K, int64_t N, size_t* byt
   if (M <= 0 || K <= 0 || N <= 0 || M % 16 || K % 16 || N % 16) return NVFP4_ERR_SHAPE;
   int64_t rc[6][2];
   ctx_shapes(M, K, N, rc);
+  for (int i = 0; i < 6; ++i) {
+    int64_t e = 0;
+    if (!mul_ok(rc[i][0], rc[i][1], &e)) return NVFP4_ERR_SHAPE;
+  }
   size_t total = 0;
   for (int i = 0; i < 6; ++i) {
     total += align256((size_t)(rc[i][0] * (rc[i][1] / 2)));   // codes

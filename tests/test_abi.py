@@ -31,9 +31,11 @@ def test_every_declared_symbol_is_exported():
 def test_tensor_bytes():
     assert nv.nvfp4_tensor_bytes(64, 256, nv.SCALE_1X16) == (64 * 128, 64 * 16)
     assert nv.nvfp4_tensor_bytes(128, 256, nv.SCALE_16X16) == (128 * 128, 8 * 16)
-    for bad in [(64, 24, 0), (0, 16, 0), (24, 32, 1), (16, 16, 5)]:
+    for bad in [(64, 24, 0), (0, 16, 0), (24, 32, 1), (16, 16, 5),
+                (1 << 40, 1 << 30, 0), ((1 << 62) // 8 + 1, 16, 0)]:   # sizes past 2^62 bytes
         with pytest.raises(nv.NVFP4Error):
             nv.nvfp4_tensor_bytes(*bad)
+    assert nv.nvfp4_tensor_bytes(1 << 30, 1 << 20, nv.SCALE_1X16)[0] == (1 << 49)
 
 
 def test_workspace_bytes_and_status_strings():
@@ -190,6 +192,8 @@ def test_bf16_gemm_and_switch_argument_errors():
 
 
 def test_linear_ctx_bytes_and_init():
+    with pytest.raises(nv.NVFP4Error):
+        nv.nvfp4_linear_ctx_bytes(1 << 40, 1 << 30, 16)   # sizes past 2^62 bytes
     """One-buffer layout of the six layer operands (host bookkeeping only)."""
     M, K, N = 64, 96, 160
     nbytes = nv.nvfp4_linear_ctx_bytes(M, K, N)
