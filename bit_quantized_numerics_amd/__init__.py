@@ -42,7 +42,8 @@ class c_tensor(ctypes.Structure):
 class c_quant_opts(ctypes.Structure):
     _fields_ = [("round", ctypes.c_int32), ("transpose", ctypes.c_int32), ("rht", ctypes.c_int32),
                 ("rht_signs", ctypes.c_uint32), ("seed", ctypes.c_uint64),
-                ("offset", ctypes.c_uint64), ("stream_id", ctypes.c_uint32)]
+                ("offset", ctypes.c_uint64), ("stream_id", ctypes.c_uint32),
+                ("rht_d", ctypes.c_int32)]
 
 
 class c_recipe(ctypes.Structure):
@@ -206,12 +207,13 @@ def _opts(round_mode=RN, transpose=False, rht=False, rht_signs=0, seed=0, offset
 
 def nvfp4_quantize(x: torch.Tensor, ws: Workspace, out: NVFP4Tensor | None = None, *,
                    round_mode=RN, transpose=False, rht=False, rht_signs=0, seed=0, offset=0,
-                   stream_id=0) -> NVFP4Tensor:
+                   stream_id=0, rht_d=16) -> NVFP4Tensor:
     rows, cols = x.shape
     if out is None:
         out = (NVFP4Tensor(cols, rows, device=x.device) if transpose
                else NVFP4Tensor(rows, cols, device=x.device))
     o = _opts(round_mode, transpose, rht, rht_signs, seed, offset, stream_id)
+    o.rht_d = rht_d
     ct = out.c()
     _check(_lib.nvfp4_quantize(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), rows, cols, _ld(x),
                                ctypes.byref(o), ctypes.byref(ct), ws.ptr, ws.nbytes,

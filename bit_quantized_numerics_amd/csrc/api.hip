@@ -89,6 +89,7 @@ nvfp4_status check_opts(const nvfp4_quant_opts* o) {
   if (o->transpose != 0 && o->transpose != 1) return NVFP4_ERR_DTYPE;
   if (o->rht != 0 && o->rht != 1) return NVFP4_ERR_DTYPE;
   if (o->rht_signs > 0xFFFFu) return NVFP4_ERR_DTYPE;
+  if (o->rht_d != 0 && o->rht_d != 4 && o->rht_d != 16) return NVFP4_ERR_DTYPE;
   if (o->offset % 16 != 0) return NVFP4_ERR_ALIGN;
   return NVFP4_OK;
 }
@@ -330,10 +331,12 @@ nvfp4_status nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t 
   a.status = ws_word(workspace, kSlotStatus);
   int flags = 0;
   const int slot = opts->rht ? kSlotQRht : kSlotQRaw;
+  const bool rht4 = opts->rht && opts->rht_d == 4;
   if (opts->transpose) {
     set_shape(out, cols, rows, NVFP4_SCALE_1X16);
     a.col = copy_args(out, workspace, slot, opts);
-    flags = kFCol | (opts->rht ? kFRht : 0) | (opts->round == NVFP4_SR ? kFSrCol : 0);
+    flags = kFCol | (opts->rht ? (rht4 ? kFRht4 : kFRht) : 0) |
+            (opts->round == NVFP4_SR ? kFSrCol : 0);
   } else {
     set_shape(out, rows, cols, NVFP4_SCALE_1X16);
     a.row = copy_args(out, workspace, slot, opts);
@@ -342,7 +345,7 @@ nvfp4_status nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t 
   NVFP4_HIP(zero_slots(workspace, kSlotQRaw, 2, s));
   NVFP4_HIP(launch_amax(x, dtype, rows, cols, ld, opts->rht_signs,
                         opts->rht ? nullptr : ws_word(workspace, kSlotQRaw),
-                        opts->rht ? ws_word(workspace, kSlotQRht) : nullptr, s));
+                        opts->rht ? ws_word(workspace, kSlotQRht) : nullptr, s, rht4 ? 4 : 16));
   NVFP4_HIP(launch_quant_tile(dtype, flags, a, s));
   return NVFP4_OK;
 }
@@ -360,6 +363,7 @@ nvfp4_status nvfp4_quantize_rowcol(const void* x, int32_t dtype, int64_t rows, i
   NVFP4_TRY(check_workspace(workspace, ws_bytes));
   if (opts_row->transpose != 0 || opts_row->rht != 0 || opts_col->transpose != 1)
     return NVFP4_ERR_SHAPE;
+  if (opts_col->rht && opts_col->rht_d == 4) return NVFP4_ERR_DTYPE;  // 16-point only here
   if (rows % 16 != 0) return NVFP4_ERR_SHAPE;
   const hipStream_t s = as_stream(stream);
   set_shape(row, rows, cols, NVFP4_SCALE_1X16);

@@ -220,4 +220,30 @@ __device__ __forceinline__ void rht16_inplace(float* u, uint32_t signs) {
   for (int i = 0; i < 16; ++i) u[i * S] = u[i * S] * 0.25f;
 }
 
+// In-place 4-point transforms y = 1/2 H4 diag(s) x on the four chunks
+// u[0..3], u[4..7], u[8..11], u[12..15] (stride S) with the same four signs
+// (bits 0-3) [Review s3; Captions Fig. 12]: signs, butterflies h = 1, 2 as
+// (a+b, a-b), x 1/2.
+template <int S>
+__device__ __forceinline__ void rht4_inplace(float* u, uint32_t signs) {
+#pragma unroll
+  for (int c = 0; c < 16; c += 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if ((signs >> i) & 1u) u[(c + i) * S] = -u[(c + i) * S];
+#pragma unroll
+    for (int h = 1; h < 4; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i & h) continue;
+        const float a = u[(c + i) * S], b = u[(c + i + h) * S];
+        u[(c + i) * S] = a + b;
+        u[(c + i + h) * S] = a - b;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[(c + i) * S] = u[(c + i) * S] * 0.5f;
+  }
+}
+
 }  // namespace nvfp4

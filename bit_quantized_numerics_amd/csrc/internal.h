@@ -16,6 +16,7 @@ constexpr int kF2D = 4;      // 16x16 blocks (weights); the column copy is the t
 constexpr int kFRht = 8;     // RHT16 along rows before the column copy
 constexpr int kFSrRow = 16;  // stochastic rounding for the row copy
 constexpr int kFSrCol = 32;  // stochastic rounding for the column copy
+constexpr int kFRht4 = 64;   // 4-point RHT along rows before the column copy (kFRht unset)
 
 // A tensor amax lives in kAmaxSlots words kAmaxStride words apart (each on
 // its own 128-byte line); its value is the max over the slots.
@@ -42,8 +43,10 @@ struct TileArgs {
 };
 
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t s);
+// rht_d: size of the transform behind out_rht (16, or 4 with out_raw null).
 hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
-                       uint32_t signs, uint32_t* out_raw, uint32_t* out_rht, hipStream_t s);
+                       uint32_t signs, uint32_t* out_raw, uint32_t* out_rht, hipStream_t s,
+                       int rht_d = 16);
 hipError_t launch_quant_tile(int dtype, int flags, const TileArgs& a, hipStream_t s);
 hipError_t launch_rht_d(const void* x, float* y, int dtype, int64_t rows, int64_t cols, int64_t ld,
                         int axis, int d, const uint32_t* signs, float c, hipStream_t s);

@@ -108,7 +108,7 @@ __device__ __forceinline__ void load_patch(const TIn* x, int64_t tile_r0, int64_
 // RHTC also the amax of the transform along rows (the Wgrad copies take their
 // scale after the transform).
 
-template <typename TIn, bool RAW, bool RHTC>
+template <typename TIn, bool RAW, bool RHTC, int RD = 16>
 __global__ __launch_bounds__(kStatsThreads) void amax_kernel(const TIn* __restrict__ x,
                                                              int64_t rows, int64_t cols, int64_t ld,
                                                              uint32_t signs, uint32_t* out_raw,
@@ -132,7 +132,12 @@ __global__ __launch_bounds__(kStatsThreads) void amax_kernel(const TIn* __restri
   }
   if (RHTC) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) rht16_inplace<8>(&v[0][j], signs);
+    for (int j = 0; j < 8; ++j) {
+      if (RD == 4)
+        rht4_inplace<8>(&v[0][j], signs);
+      else
+        rht16_inplace<8>(&v[0][j], signs);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
@@ -165,10 +170,16 @@ __global__ __launch_bounds__(kStatsThreads) void amax_kernel(const TIn* __restri
 template <typename TIn>
 static hipError_t amax_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ld,
                                 uint32_t signs, uint32_t* out_raw, uint32_t* out_rht,
-                                hipStream_t s) {
+                                hipStream_t s, int rht_d) {
   const dim3 grid((unsigned)((cols + kTileC - 1) / kTileC),
                   (unsigned)((rows + kStatsTileR - 1) / kStatsTileR));
   const TIn* p = static_cast<const TIn*>(x);
+  if (rht_d == 4) {
+    if (out_raw || !out_rht) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((amax_kernel<TIn, false, true, 4>), grid, dim3(kStatsThreads), 0, s, p, rows,
+                       cols, ld, signs, out_raw, out_rht);
+    return hipGetLastError();
+  }
   if (out_raw && out_rht)
     hipLaunchKernelGGL((amax_kernel<TIn, true, true>), grid, dim3(kStatsThreads), 0, s, p, rows, cols,
                        ld, signs, out_raw, out_rht);
@@ -182,9 +193,11 @@ static hipError_t amax_dispatch(const void* x, int64_t rows, int64_t cols, int64
 }
 
 hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
-                       uint32_t signs, uint32_t* out_raw, uint32_t* out_rht, hipStream_t s) {
-  if (dtype == kDtypeBF16) return amax_dispatch<uint16_t>(x, rows, cols, ld, signs, out_raw, out_rht, s);
-  return amax_dispatch<float>(x, rows, cols, ld, signs, out_raw, out_rht, s);
+                       uint32_t signs, uint32_t* out_raw, uint32_t* out_rht, hipStream_t s,
+                       int rht_d) {
+  if (dtype == kDtypeBF16)
+    return amax_dispatch<uint16_t>(x, rows, cols, ld, signs, out_raw, out_rht, s, rht_d);
+  return amax_dispatch<float>(x, rows, cols, ld, signs, out_raw, out_rht, s, rht_d);
 }
 
 // ---------------------------------------------------------------- emit
@@ -233,7 +246,7 @@ template <typename TIn, int F>
 __global__ __launch_bounds__(2 * emit_rows(F)) void quant_tile_kernel(TileArgs a) {
   constexpr int TR = emit_rows(F);
   constexpr bool ROW = F & kFRow, COL = F & kFCol, TWO_D = F & kF2D, RHT = F & kFRht;
-  constexpr bool SR_ROW = F & kFSrRow, SR_COL = F & kFSrCol;
+  constexpr bool SR_ROW = F & kFSrRow, SR_COL = F & kFSrCol, RHT4 = F & kFRht4;
 
   const int t = threadIdx.x, cg = t & 31, rs = t >> 5;
   const int64_t rows = a.rows, cols = a.cols;
@@ -334,6 +347,7 @@ __global__ __launch_bounds__(2 * emit_rows(F)) void quant_tile_kernel(TileArgs a
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (RHT) rht16_inplace<8>(&v[0][j], a.signs);
+        if (RHT4) rht4_inplace<8>(&v[0][j], a.signs);
         float am = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) am = fmaxf(am, __builtin_fabsf(v[i][j]));
@@ -383,6 +397,8 @@ static bool tile_dispatch(int flags, const TileArgs& a, hipStream_t s) {
     NVFP4_CASE(kFCol | kFSrCol)
     NVFP4_CASE(kFCol | kFRht)
     NVFP4_CASE(kFCol | kFRht | kFSrCol)
+    NVFP4_CASE(kFCol | kFRht4)
+    NVFP4_CASE(kFCol | kFRht4 | kFSrCol)
     NVFP4_CASE(kFRow | kFCol)
     NVFP4_CASE(kFRow | kFCol | kFRht)
     NVFP4_CASE(kFRow | kFCol | kFSrRow | kFSrCol)

@@ -102,7 +102,11 @@ typedef struct {
  *              stochastic-rounding draw of operand element (r, c) comes from
  *              the Philox4x32-10 counter-based generator with key = seed,
  *              counter = (e/8, stream_id, 0), e = offset + r*C + c in the
- *              operand's own [R, C] layout; offset % 16 == 0. */
+ *              operand's own [R, C] layout; offset % 16 == 0.
+ *   rht_d      size of the transform with rht: 0 or 16 (the recipe), or 4
+ *              (four 4-point transforms y = 1/2 H4 diag(s) x per 16-element
+ *              chunk, signs bits 0-3 [Captions Fig. 12]; nvfp4_quantize only).
+ *              Any other value is NVFP4_ERR_DTYPE. */
 typedef struct {
   int32_t round;
   int32_t transpose;
@@ -111,6 +115,7 @@ typedef struct {
   uint64_t seed;
   uint64_t offset;
   uint32_t stream_id;
+  int32_t rht_d;
 } nvfp4_quant_opts;
 
 /* The layer recipe.  All-zero switches give the pages' recipe [Review "Core
@@ -214,7 +219,8 @@ nvfp4_status nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t 
  * nvfp4_quantize_rowcol: both copies an operand needs for a training step
  * from one read of x [rows, cols]: `row` = x with 1x16 blocks along cols
  * (opts_row; transpose/rht must be 0) and `col` = (R x)^T with 1x16 blocks
- * along rows (opts_col; transpose must be 1, rht optional).  Each copy has its
+ * along rows (opts_col; transpose must be 1, rht optional with rht_d 0 or
+ * 16; rht_d 4 is NVFP4_ERR_DTYPE here).  Each copy has its
  * own tensor scale.  Equivalent to two nvfp4_quantize calls.  [Review s6
  * steps 1-3; Captions Fig. 5]
  */

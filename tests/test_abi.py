@@ -84,8 +84,22 @@ def test_quantize_argument_errors():
     assert _q(opts=nv.c_quant_opts(2, 0, 0, 0, 0, 0, 0)) == nv.ERR_DTYPE
     assert _q(opts=nv.c_quant_opts(1, 0, 0, 0, 0, 8, 0)) == nv.ERR_ALIGN       # offset % 16
     assert _q(opts=nv.c_quant_opts(0, 0, 1, 0, 0, 0, 0)) == nv.ERR_SHAPE       # RHT needs transpose
+    assert _q(opts=nv.c_quant_opts(0, 1, 1, 0, 0, 0, 0, 8)) == nv.ERR_DTYPE    # RHT size 8
     assert _q(rows=40, opts=nv.c_quant_opts(0, 1, 0, 0, 0, 0, 0)) == nv.ERR_SHAPE
     assert _q(opts=nv.c_quant_opts(0, 1, 1, 0x10000, 0, 0, 0)) == nv.ERR_DTYPE
+
+
+def test_rowcol_takes_only_the_16_point_transform():
+    o_r = nv.c_quant_opts(0, 0, 0, 0, 0, 0, 0)
+    o_c = nv.c_quant_opts(0, 1, 1, 0, 0, 0, 1, 4)
+    r, c = _tensor(), _tensor()
+    assert nv._lib.nvfp4_quantize_rowcol(P, nv.BF16, 64, 256, 256, ctypes.byref(o_r),
+                                         ctypes.byref(o_c), ctypes.byref(r), ctypes.byref(c), P,
+                                         WSB, None) == nv.ERR_DTYPE
+    o_c.rht_d = 16
+    assert nv._lib.nvfp4_quantize_rowcol(P, nv.BF16, 64, 256, 256, ctypes.byref(o_r),
+                                         ctypes.byref(o_c), ctypes.byref(r), ctypes.byref(c), None,
+                                         WSB, None) == nv.ERR_WORKSPACE
 
 
 def test_gemm_argument_errors():

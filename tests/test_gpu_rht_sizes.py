@@ -56,3 +56,29 @@ def test_wgrad_operand_with_other_size(nv, d):
     q = nv.nvfp4_quantize(y, ws, transpose=True)
     ref = O.quantize(O.rht(x.float().numpy(), 0, d, np.array(signs, np.uint32)), transpose=True)
     assert_q_equal(q, ref, f"wgrad operand d={d}")
+
+
+# (rows, cols): several 128-row emit tiles with a ragged column tile; a single
+# 16-token chunk row; odd tile counts.
+@pytest.mark.parametrize("rows,cols", [(512, 400), (16, 256), (272, 48)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("sr", [False, True])
+def test_fused_d4_quantise(nv, rows, cols, dtype, sr):
+    """The 4-point transform fused into the quantiser (rht_d = 4): equal, code
+    for code, to the oracle's separate 4-point transform along tokens followed
+    by its quantisation of the transpose (the fused kernel computes the same
+    fp32 values in registers)."""
+    g = torch.Generator().manual_seed(rows + cols)
+    x = (torch.randn(rows, cols, generator=g) * 2.0).to(dtype)
+    x[0, :] *= 40.0  # an outlier row
+    signs = nv.nvfp4_rht_signs128_from_seed(7)
+    s16 = int(signs[0]) & 0xFFFF
+    ws = nv.Workspace("cuda")
+    nv.nvfp4_workspace_init(ws)
+    say("fused d4", rows, cols, dtype, sr)
+    q = nv.nvfp4_quantize(x.cuda(), ws, transpose=True, rht=True, rht_d=4, rht_signs=s16,
+                          round_mode=nv.SR if sr else nv.RN, seed=1234, stream_id=1)
+    y = O.rht(x.float().numpy(), 0, 4, np.array(signs, np.uint32))
+    ref = O.quantize(y, transpose=True, sr=sr, seed=1234, stream=1)
+    assert_q_equal(q, ref, f"fused d4 {rows}x{cols} {dtype} sr={sr}")
+    assert nv.nvfp4_device_status(ws) == nv.OK
