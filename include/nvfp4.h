@@ -162,13 +162,18 @@ typedef struct {
 
 /* ------------------------------------------------------------ size queries */
 
-/* Bytes of the codes and scales arrays of a [rows, cols] operand. */
+/* Bytes of the codes and scales arrays of a [rows, cols] operand (codes
+ * rows * cols / 2; scales per block: rows * cols / 16 for 1x16, / 256 for
+ * 16x16, / 32 for MX32).  cols % 16 (MX32: % 32) and, for 16x16, rows % 16
+ * must hold and the byte counts stay below 2^62, else NVFP4_ERR_SHAPE; an
+ * unknown scale_mode is NVFP4_ERR_DTYPE. */
 nvfp4_status nvfp4_tensor_bytes(int64_t rows, int64_t cols, int32_t scale_mode,
                                 size_t* codes_bytes, size_t* scales_bytes);
 
 /* Bytes of one device buffer that holds all six quantised operands of a
  * layer step (the buffers of nvfp4_linear_ctx), for nvfp4_linear_ctx_init.
- * M, K, N positive multiples of 16. */
+ * M, K, N positive multiples of 16 whose operand sizes stay below 2^62
+ * bytes, else NVFP4_ERR_SHAPE. */
 nvfp4_status nvfp4_linear_ctx_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes);
 
 /* Point ctx's six operands into `buffer` (a device buffer of at least
