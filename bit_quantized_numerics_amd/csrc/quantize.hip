@@ -13,7 +13,8 @@
 //     lane's row (lane ^ 1 holds the other 8 columns);
 //   - a 1x16 block along rows (the column-wise copy the backward GEMMs need,
 //     [Review s2]) is one column of the patch, which is also exactly one
-//     16-token chunk of the random Hadamard transform [Review s3];
+//     16-token chunk of the random Hadamard transform [Review s3] (or four
+//     4-token chunks of the size-4 transform [Captions Fig. 12]);
 //   - a 16x16 weight tile is the patch plus its neighbour lane's patch.
 // Reads are 16-byte loads, 16 per thread in flight.  Every row of the row-wise
 // copy is written as 128 contiguous bytes per tile.  Each 16-element column
@@ -106,7 +107,8 @@ __device__ __forceinline__ void load_patch(const TIn* x, int64_t tile_r0, int64_
 // Tensor amax [Review s1 Step 1] as the largest |x| bit pattern (Inf/NaN sort
 // above every finite value, so a non-finite input is never lost), and with
 // RHTC also the amax of the transform along rows (the Wgrad copies take their
-// scale after the transform).
+// scale after the transform): RD = 16, or RD = 4 (four 4-point transforms per
+// 16-row patch column, the Hadamard-size ablation).
 
 template <typename TIn, bool RAW, bool RHTC, int RD = 16>
 __global__ __launch_bounds__(kStatsThreads) void amax_kernel(const TIn* __restrict__ x,
