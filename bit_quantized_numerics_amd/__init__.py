@@ -70,6 +70,8 @@ _SIGS = {
     "nvfp4_status_string": (ctypes.c_char_p, [_i32]),
     "nvfp4_quantize": (_i32, [_vp, _i32, _i64, _i64, _i64, ctypes.POINTER(c_quant_opts), _T, _vp,
                               _sz, _vp]),
+    "nvfp4_quantize_static": (_i32, [_vp, _i32, _i64, _i64, _i64, ctypes.POINTER(c_quant_opts), _T,
+                                     _vp, _vp]),
     "nvfp4_quantize_rowcol": (_i32, [_vp, _i32, _i64, _i64, _i64, ctypes.POINTER(c_quant_opts),
                                      ctypes.POINTER(c_quant_opts), _T, _T, _vp, _sz, _vp]),
     "nvfp4_quantize_2d": (_i32, [_vp, _i32, _i64, _i64, _i64, _T, _T, _vp, _sz, _vp]),
@@ -218,6 +220,27 @@ def nvfp4_quantize(x: torch.Tensor, ws: Workspace, out: NVFP4Tensor | None = Non
     _check(_lib.nvfp4_quantize(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), rows, cols, _ld(x),
                                ctypes.byref(o), ctypes.byref(ct), ws.ptr, ws.nbytes,
                                _stream(x.device)), "nvfp4_quantize")
+    out.update(ct)
+    return out
+
+
+def nvfp4_quantize_static(x: torch.Tensor, status: torch.Tensor, out: NVFP4Tensor | None = None, *,
+                          round_mode=RN, transpose=False, rht=False, rht_signs=0, seed=0, offset=0,
+                          stream_id=0, rht_d=16) -> NVFP4Tensor:
+    """nvfp4_quantize without a workspace (library-owned reduction slots);
+    `status`: a device int32/uint32 tensor of one element that receives
+    ERR_NONFINITE when the amax is not finite."""
+    rows, cols = x.shape
+    if out is None:
+        out = (NVFP4Tensor(cols, rows, device=x.device) if transpose
+               else NVFP4Tensor(rows, cols, device=x.device))
+    o = _opts(round_mode, transpose, rht, rht_signs, seed, offset, stream_id)
+    o.rht_d = rht_d
+    ct = out.c()
+    _check(_lib.nvfp4_quantize_static(ctypes.c_void_p(x.data_ptr()), _dtype_code(x), rows, cols,
+                                      _ld(x), ctypes.byref(o), ctypes.byref(ct),
+                                      ctypes.c_void_p(status.data_ptr()), _stream(x.device)),
+           "nvfp4_quantize_static")
     out.update(ct)
     return out
 

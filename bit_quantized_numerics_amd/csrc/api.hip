@@ -12,6 +12,14 @@
 #include "internal.h"
 
 #include <cmath>
+#include <mutex>
+
+// Reduction slots of nvfp4_quantize_static: a fixed 8 KB (two tensor-amax
+// regions) per GPU, whatever the input size.  Host code never uses this name
+// as an address (on the host it is only a stand-in): each device's copy is
+// reached through hipGetSymbolAddress, once per device, and that pointer is
+// what the kernels receive.
+static __device__ __align__(256) uint32_t scratch[2 * nvfp4::kAmaxRegionWords];
 
 namespace {
 
@@ -188,6 +196,89 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// ---- nvfp4_quantize and its allocation-free variant
+
+nvfp4_status check_quantize_args(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                 int64_t ld, const nvfp4_quant_opts* opts,
+                                 const nvfp4_tensor* out) {
+  NVFP4_TRY(check_source(x, dtype, rows, cols, ld));
+  NVFP4_TRY(check_opts(opts));
+  NVFP4_TRY(check_out(out));
+  // The RHT runs along the operand's block axis; the recipe applies it to the
+  // column-wise (token-axis) Wgrad copies only [Review s3], which is the
+  // supported placement.
+  if (opts->rht && !opts->transpose) return NVFP4_ERR_SHAPE;
+  if (opts->transpose && rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+// Enqueues the amax pass and the emit pass of one quantisation; `slots` is
+// two consecutive amax regions (plain amax, then amax after the RHT) and
+// `status` the word a non-finite amax is reported in.
+nvfp4_status quantize_enqueue(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                              const nvfp4_quant_opts* opts, nvfp4_tensor* out, uint32_t* slots,
+                              uint32_t* status, hipStream_t s) {
+  uint32_t* slot_raw = slots;
+  uint32_t* slot_rht = slots + kAmaxRegionWords;
+  TileArgs a;
+  a.x = x;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.signs = opts->rht_signs;
+  a.status = status;
+  uint32_t* slot = opts->rht ? slot_rht : slot_raw;
+  const bool rht4 = opts->rht && opts->rht_d == 4;
+  int flags = 0;
+  CopyArgs c;
+  c.codes = out->codes;
+  c.scales = out->scales;
+  c.global = out->global_scale;
+  c.amax = slot;
+  c.seed = opts->seed;
+  c.offset = opts->offset;
+  c.stream = opts->stream_id;
+  if (opts->transpose) {
+    set_shape(out, cols, rows, NVFP4_SCALE_1X16);
+    a.col = c;
+    flags = kFCol | (opts->rht ? (rht4 ? kFRht4 : kFRht) : 0) |
+            (opts->round == NVFP4_SR ? kFSrCol : 0);
+  } else {
+    set_shape(out, rows, cols, NVFP4_SCALE_1X16);
+    a.row = c;
+    flags = kFRow | (opts->round == NVFP4_SR ? kFSrRow : 0);
+  }
+  NVFP4_HIP(launch_zero_words(slots, 2 * kAmaxRegionWords, s));
+  NVFP4_HIP(launch_amax(x, dtype, rows, cols, ld, opts->rht_signs, opts->rht ? nullptr : slot_raw,
+                        opts->rht ? slot_rht : nullptr, s, rht4 ? 4 : 16));
+  NVFP4_HIP(launch_quant_tile(dtype, flags, a, s));
+  return NVFP4_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch` (the stream's device must be the current
+// one); looked up on the first call on each device and kept until the
+// process ends.
+nvfp4_status static_scratch(hipStream_t s, uint32_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_HIP;
+  if (s) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess || sdev != dev) return NVFP4_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NVFP4_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,43 +402,21 @@ const char* nvfp4_status_string(nvfp4_status s) {
 nvfp4_status nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
                             const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* workspace,
                             size_t ws_bytes, void* stream) {
-  NVFP4_TRY(check_source(x, dtype, rows, cols, ld));
-  NVFP4_TRY(check_opts(opts));
-  NVFP4_TRY(check_out(out));
+  NVFP4_TRY(check_quantize_args(x, dtype, rows, cols, ld, opts, out));
   NVFP4_TRY(check_workspace(workspace, ws_bytes));
-  // The RHT runs along the operand's block axis; the recipe applies it to the
-  // column-wise (token-axis) Wgrad copies only [Review s3], which is the
-  // supported placement.
-  if (opts->rht && !opts->transpose) return NVFP4_ERR_SHAPE;
-  if (opts->transpose && rows % 16 != 0) return NVFP4_ERR_SHAPE;
-  const hipStream_t s = as_stream(stream);
+  return quantize_enqueue(x, dtype, rows, cols, ld, opts, out, ws_word(workspace, kSlotQRaw),
+                          ws_word(workspace, kSlotStatus), as_stream(stream));
+}
 
-  TileArgs a;
-  a.x = x;
-  a.rows = rows;
-  a.cols = cols;
-  a.ld = ld;
-  a.signs = opts->rht_signs;
-  a.status = ws_word(workspace, kSlotStatus);
-  int flags = 0;
-  const int slot = opts->rht ? kSlotQRht : kSlotQRaw;
-  const bool rht4 = opts->rht && opts->rht_d == 4;
-  if (opts->transpose) {
-    set_shape(out, cols, rows, NVFP4_SCALE_1X16);
-    a.col = copy_args(out, workspace, slot, opts);
-    flags = kFCol | (opts->rht ? (rht4 ? kFRht4 : kFRht) : 0) |
-            (opts->round == NVFP4_SR ? kFSrCol : 0);
-  } else {
-    set_shape(out, rows, cols, NVFP4_SCALE_1X16);
-    a.row = copy_args(out, workspace, slot, opts);
-    flags = kFRow | (opts->round == NVFP4_SR ? kFSrRow : 0);
-  }
-  NVFP4_HIP(zero_slots(workspace, kSlotQRaw, 2, s));
-  NVFP4_HIP(launch_amax(x, dtype, rows, cols, ld, opts->rht_signs,
-                        opts->rht ? nullptr : ws_word(workspace, kSlotQRaw),
-                        opts->rht ? ws_word(workspace, kSlotQRht) : nullptr, s, rht4 ? 4 : 16));
-  NVFP4_HIP(launch_quant_tile(dtype, flags, a, s));
-  return NVFP4_OK;
+nvfp4_status nvfp4_quantize_static(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                   int64_t ld, const nvfp4_quant_opts* opts, nvfp4_tensor* out,
+                                   uint32_t* status, void* stream) {
+  NVFP4_TRY(check_quantize_args(x, dtype, rows, cols, ld, opts, out));
+  if (!status) return NVFP4_ERR_NULL;
+  if (!aligned(status, 4)) return NVFP4_ERR_ALIGN;
+  uint32_t* slots = nullptr;
+  NVFP4_TRY(static_scratch(as_stream(stream), &slots));
+  return quantize_enqueue(x, dtype, rows, cols, ld, opts, out, slots, status, as_stream(stream));
 }
 
 nvfp4_status nvfp4_quantize_rowcol(const void* x, int32_t dtype, int64_t rows, int64_t cols,

@@ -23,7 +23,8 @@
  *
  * Conventions for every call:
  *   - All data pointers are DEVICE pointers; the caller owns every buffer.
- *     The library never allocates device memory and keeps no global state.
+ *     The library never allocates device memory; its only global state is
+ *     the per-device scratch of nvfp4_quantize_static.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work on it and return; none synchronises except
  *     nvfp4_device_status().
@@ -219,6 +220,28 @@ const char* nvfp4_status_string(nvfp4_status s);
 nvfp4_status nvfp4_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols,
                             int64_t ld, const nvfp4_quant_opts* opts, nvfp4_tensor* out,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_quantize_static: nvfp4_quantize for callers that cannot allocate or
+ * hand over a workspace -- code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The operation, the arguments shared with
+ * nvfp4_quantize and their errors are those of nvfp4_quantize; the call
+ * allocates nothing and enqueues the same kernels.  Differences:
+ *   - the tensor-amax reduction slots live in a library-owned device array
+ *     of a fixed 8 KB per GPU, whatever the input size (so no input is too
+ *     large for it); each GPU's copy is looked up (hipGetSymbolAddress) on
+ *     the first call on that device and is held until the process ends;
+ *   - status: caller-owned device word (4-byte aligned, not NULL, else
+ *     NVFP4_ERR_NULL / NVFP4_ERR_ALIGN); a non-finite amax raises it to
+ *     NVFP4_ERR_NONFINITE (atomic max), nothing ever clears it;
+ *   - the stream must belong to the current device, else NVFP4_ERR_HIP.
+ * Every call on one GPU shares that GPU's array: calls issued in order on one
+ * stream are safe, calls that overlap on one GPU (two streams, two host
+ * threads without ordering) race and give wrong scales.
+ */
+nvfp4_status nvfp4_quantize_static(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                   int64_t ld, const nvfp4_quant_opts* opts, nvfp4_tensor* out,
+                                   uint32_t* status, void* stream);
 
 /*
  * nvfp4_quantize_rowcol: both copies an operand needs for a training step

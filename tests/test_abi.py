@@ -243,3 +243,17 @@ def test_peak_helper_argument_errors():
     assert f(100, 0, None, ctypes.byref(flops), None) == nv.ERR_NULL
     assert f(100, 0, P, None, None) == nv.ERR_NULL
     assert f(0, 0, P, ctypes.byref(flops), None) == nv.ERR_SHAPE
+
+
+def test_quantize_static_argument_errors():
+    """Argument errors of the allocation-free variant come back before any
+    HIP call (and so before the per-device scratch is looked up)."""
+    f = nv._lib.nvfp4_quantize_static
+    o = nv.c_quant_opts(0, 0, 0, 0, 0, 0, 0)
+    t = _tensor()
+    assert f(None, nv.BF16, 64, 256, 256, ctypes.byref(o), ctypes.byref(t), P, None) == nv.ERR_NULL
+    assert f(P, nv.BF16, 64, 256, 256, ctypes.byref(o), ctypes.byref(t), None, None) == nv.ERR_NULL
+    assert f(P, nv.BF16, 64, 256, 256, ctypes.byref(o), ctypes.byref(t), P + 2, None) == nv.ERR_ALIGN
+    assert f(P, nv.BF16, 64, 24, 24, ctypes.byref(o), ctypes.byref(t), P, None) == nv.ERR_SHAPE
+    bad = nv.c_quant_opts(0, 0, 1, 0, 0, 0, 0)   # RHT without transpose
+    assert f(P, nv.BF16, 64, 256, 256, ctypes.byref(bad), ctypes.byref(t), P, None) == nv.ERR_SHAPE
