@@ -44,7 +44,7 @@ BYTES_2D = 2.0 + 2 * (0.5 + 1.0 / 256)
 # 1 GiB device copy reads back), averaged over the single Fprop, Dgrad and
 # Wgrad launches: 1066.3, 874.1 and 1287.9 MB.  Valid only for the kernel
 # source it was measured on (profiles/hbm_traffic_gemm_quantize_*.md).
-GEMM_TRAFFIC = {"source_sha1": "79eb56f995e70372b7d5c4e1eca99b892bfd0083",
+GEMM_TRAFFIC = {"source_sha1": "0783a32993c9790cf80729407642f8e36e78d602",
                 "bytes_per_launch": 1076.1e6}
 
 
@@ -81,9 +81,21 @@ def copy_reference(mib: int) -> None:
                       "bytes_written_per_launch": n * 4}), flush=True)
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(sample_tokens: int):
     """The oracle, as it stands, on a bounded sample of the same step: the
-    layer with `sample_tokens` tokens (W stays full size)."""
+    layer with `sample_tokens` tokens (W stays full size): the six
+    quantisations, then the three products C = deq(A) deq(B)^T (float64)."""
     import oracle as O
     import workloads as W
     Ms = sample_tokens
@@ -96,14 +108,15 @@ def cpu_baseline(sample_tokens: int):
     ops = O.linear_operands(x, w, dy, O.Recipe(rht_signs=signs, sr_seed=W.SR_SEED))
     t1 = time.perf_counter()
     for a, b in (("xq", "wq"), ("dyq", "wqt"), ("dyqt", "xqt")):
-        O.gemm(ops[a], ops[b])
+        O.gemm_c(ops[a], ops[b])
     t2 = time.perf_counter()
     flops = 3 * 2.0 * Ms * N * K
     qbytes = BYTES_ROWCOL * (Ms * K + Ms * N) + BYTES_2D * N * K
     return {
         "value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "cpu_model": _cpu_model(), "cpus_online": os.cpu_count(),
         "sample": f"one layer step at {Ms} tokens (K={K}, N={N}, W full size): all six "
-                  f"quantisations + three float64 GEMMs; {t2 - t0:.2f} s",
+                  f"quantisations + three float64 products C = deq(A) deq(B)^T; {t2 - t0:.2f} s",
         "quantize_GBps": qbytes / (t1 - t0) / 1e9,
     }
 
@@ -369,18 +382,19 @@ def main():
     # memory traffic), next to the datasheet peak used in `roofline`
     nv.nvfp4_peak_mfma_f16(1000)
     mfma_loop = nv.nvfp4_peak_mfma_f16(5000)
-    mfma_5bit = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0x87C087C0)
+    mfma_6bit = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0x87E087E0)
     mfma_const = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0)
     out["measured_ceiling"] = {
         "mfma_f16_loop_TFLOPs": round(mfma_loop, 1),
-        "mfma_f16_loop_5bit_operands_TFLOPs": round(mfma_5bit, 1),
+        "mfma_f16_loop_6bit_operands_TFLOPs": round(mfma_6bit, 1),
         "mfma_f16_loop_constant_operands_TFLOPs": round(mfma_const, 1),
         "gemm_frac_of_loop": round(achieved / mfma_loop, 4),
-        "gemm_frac_of_5bit_loop": round(achieved / mfma_5bit, 4),
+        "gemm_frac_of_6bit_loop": round(achieved / mfma_6bit, 4),
         "note": "fp16 MFMA-only loop shaped like the GEMM's (16 accumulators per wave, 4 VALU per "
                 "MFMA): operands changing every iteration in sign, one exponent bit and all "
-                "mantissa bits; in sign, that exponent bit and the top 4 mantissa bits (the bit "
-                "pattern of dequantised E2M1 x E4M3 values); and constant operands"}
+                "mantissa bits; in sign, that exponent bit and the top 5 mantissa bits (the bit "
+                "pattern of dequantised E2M1 x E4M3 values, at most 6 significant bits); and "
+                "constant operands"}
     out["layer_16384_tokens"] = layer_at(nv, W, 2 * M, signs, max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)

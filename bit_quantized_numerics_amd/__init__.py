@@ -55,7 +55,8 @@ class c_recipe(ctypes.Structure):
 class c_linear_ctx(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("xq", c_tensor), ("wq", c_tensor), ("wqt", c_tensor), ("xqt", c_tensor),
-                ("dyq", c_tensor), ("dyqt", c_tensor)]
+                ("dyq", c_tensor), ("dyqt", c_tensor), ("rht_signs", ctypes.c_uint32),
+                ("rht", ctypes.c_int32)]
 
 
 _vp, _i64, _i32, _u32, _u64, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,

@@ -350,6 +350,8 @@ nvfp4_status nvfp4_linear_ctx_init(nvfp4_linear_ctx* ctx, void* buffer, size_t b
   ctx->M = M;
   ctx->K = K;
   ctx->N = N;
+  ctx->rht_signs = 0;
+  ctx->rht = 0;
   return NVFP4_OK;
 }
 
@@ -634,6 +636,8 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
     fx |= kFRow;
   }
   const bool x_rht = recipe->training && !recipe->no_rht;
+  ctx->rht_signs = recipe->rht_signs;
+  ctx->rht = x_rht ? 1 : 0;
   if (recipe->training) {
     set_shape(&ctx->xqt, K, M, NVFP4_SCALE_1X16);
     // without the RHT the column copy has the row copy's amax
@@ -689,6 +693,9 @@ nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* c
   NVFP4_TRY(check_gemm_operand(&ctx->wqt));
   NVFP4_TRY(check_gemm_operand(&ctx->xqt));
   if (recipe->rht_signs > 0xFFFFu) return NVFP4_ERR_DTYPE;
+  // (R dY)^T must carry the transform (R X)^T was built with [Review s3]
+  if ((recipe->no_rht ? 0 : 1) != ctx->rht || (ctx->rht && recipe->rht_signs != ctx->rht_signs))
+    return NVFP4_ERR_SHAPE;
   NVFP4_TRY(check_workspace(workspace, ws_bytes));
   if (!aligned(dx, 4) || !aligned(dw, 4)) return NVFP4_ERR_ALIGN;
   const hipStream_t s = as_stream(stream);

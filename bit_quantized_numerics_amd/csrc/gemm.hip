@@ -11,7 +11,8 @@
 // scale per 32 elements, so it cannot apply NVFP4's E4M3 scale per 16
 // elements without masking 3/4 of every instruction.  Instead each element is
 // dequantised exactly to fp16: q has 2 significant bits and d 4, so q*d has at
-// most 5 and lies in [2^-10, 2688], which fp16 represents exactly.  The
+// most 6 (1.5 x 1.875 = 10.1101b) and lies in [2^-10, 2688], which fp16 (11
+// significant bits, normal from 2^-14) represents exactly.  The
 // products then run on the dense fp16 MFMA (v_mfma_f32_32x32x16_f16, FP32
 // accumulate) and the epilogue multiplies by g_A g_B.
 //

@@ -564,7 +564,7 @@ hipError_t launch_rht_d(const void* x, float* y, int dtype, int64_t rows, int64_
 // ---------------------------------------------------------------- dequantise
 
 // x_hat = e2m1(code) * d_b * g [Review s1 Step 3] (NVFP4 modes) or
-// e2m1(code) * 2^(s - 127) (MXFP4), in fp32: e2m1 * d_b is exact (at most 5
+// e2m1(code) * 2^(s - 127) (MXFP4), in fp32: e2m1 * d_b is exact (at most 6
 // significant bits), so each output is the exact product rounded once.  One
 // thread per 8 consecutive elements of a row.  mode: 0 1x16, 1 16x16, 2 MX32.
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,

@@ -159,6 +159,11 @@ typedef struct {
 typedef struct {
   int64_t M, K, N;
   nvfp4_tensor xq, wq, wqt, xqt, dyq, dyqt;
+  /* Set by nvfp4_linear_fwd: the sign diagonal and whether the RHT was
+   * applied to xqt, so that the backward can refuse a recipe whose dY^T copy
+   * would get another transform than X^T (dW = (R dY)^T (R X) needs one R). */
+  uint32_t rht_signs;
+  int32_t rht;
 } nvfp4_linear_ctx;
 
 /* ------------------------------------------------------------ size queries */
@@ -379,7 +384,9 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
  * (ctx->dyq) and (R dY)^T with the RHT along tokens, SR stream 1
  * (ctx->dyqt), both with key sr_seed; then Dgrad dX = dyq . wqt^T (bf16
  * [M, K]) and Wgrad dW = dyqt . xqt^T ([N, K], dw_dtype F32 or BF16).
- * Requires a preceding nvfp4_linear_fwd with recipe->training on ctx.
+ * Requires a preceding nvfp4_linear_fwd with recipe->training on ctx, and a
+ * recipe with that forward's rht_signs and no_rht (else NVFP4_ERR_SHAPE:
+ * the two Wgrad operands must carry the same transform [Review s3]).
  */
 nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* ctx, void* dx,
                               void* dw, int32_t dw_dtype, uint64_t sr_seed,

@@ -266,6 +266,14 @@ def gemm(a: QTensor, b: QTensor):
     return ah @ bh.T, np.abs(ah) @ np.abs(bh).T
 
 
+def gemm_c(a: QTensor, b: QTensor) -> np.ndarray:
+    """C = deq(A) . deq(B)^T alone (the product of gemm() without the
+    tolerance sum S)."""
+    if a.cols != b.cols:
+        raise OracleError(ERR_SHAPE)
+    return dequant(a) @ dequant(b).T
+
+
 def gemm_entries(a_hat: np.ndarray, b_hat: np.ndarray, ms, ns):
     """Selected entries of deq(A) . deq(B)^T, one dot product each."""
     a_hat = np.ascontiguousarray(a_hat, dtype=np.float64)

@@ -257,3 +257,26 @@ def test_quantize_static_argument_errors():
     assert f(P, nv.BF16, 64, 24, 24, ctypes.byref(o), ctypes.byref(t), P, None) == nv.ERR_SHAPE
     bad = nv.c_quant_opts(0, 0, 1, 0, 0, 0, 0)   # RHT without transpose
     assert f(P, nv.BF16, 64, 256, 256, ctypes.byref(bad), ctypes.byref(t), P, None) == nv.ERR_SHAPE
+
+
+def test_backward_refuses_another_rht_than_its_forward():
+    """The Wgrad operands (R dY)^T and (R X)^T need one transform: a backward
+    recipe with other signs, or with the RHT switched on or off against the
+    forward's, is refused before anything is enqueued."""
+    M, K, N = 64, 96, 160
+    ctx = nv.c_linear_ctx()
+    nbytes = nv.nvfp4_linear_ctx_bytes(M, K, N)
+    assert nv._lib.nvfp4_linear_ctx_init(ctypes.byref(ctx), P, nbytes, M, K, N) == nv.OK
+    assert (ctx.rht_signs, ctx.rht) == (0, 0)
+    ctx.rht_signs, ctx.rht = 0x1234, 1          # what a training forward records
+    bwd = nv._lib.nvfp4_linear_bwd
+    for rec, want in ((nv.c_recipe(0x1235, 1), nv.ERR_SHAPE),           # other signs
+                      (nv.c_recipe(0x1234, 1, 0, 1), nv.ERR_SHAPE),      # RHT off
+                      (nv.c_recipe(0x1234, 1), nv.ERR_WORKSPACE)):       # matches: next check
+        assert bwd(P, nv.BF16, ctypes.byref(ctx), P, P, nv.F32, 1, ctypes.byref(rec), None, 0,
+                   None) == want
+    ctx.rht = 0                                 # forward ran with no_rht
+    assert bwd(P, nv.BF16, ctypes.byref(ctx), P, P, nv.F32, 1, ctypes.byref(nv.c_recipe(0x1234, 1)),
+               None, 0, None) == nv.ERR_SHAPE
+    assert bwd(P, nv.BF16, ctypes.byref(ctx), P, P, nv.F32, 1,
+               ctypes.byref(nv.c_recipe(0x1234, 1, 0, 1)), None, 0, None) == nv.ERR_WORKSPACE

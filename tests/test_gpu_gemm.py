@@ -48,14 +48,28 @@ def _quant_pair(nv, ws, a_np, b_np, mode_a, mode_b):
 
 
 def test_tiny_config(nv, ws):
-    """A [64, 256] 1x16 RN, B [128, 256] 16x16 RN, C = deq(A) deq(B)^T."""
+    """The tiny configuration in full: A [64, 256] 1x16 RN, B [128, 256]
+    16x16 RN, C = deq(A) deq(B)^T; the same A quantised with stochastic
+    rounding (Philox seed 1234, stream 0); and RHT16 of A along K (signs
+    from seed 0) -- codes, scales and transformed values bit for bit."""
+    from tests.gpu_util import assert_q_equal
     a, b = W.tiny_pair()
     say("gemm tiny config")
     (qa, ra), (qb, rb) = _quant_pair(nv, ws, np32(a), np32(b), 0, 1)
+    assert_q_equal(qa, ra, "tiny A")
+    assert_q_equal(qb, rb, "tiny B")
     C, S = O.gemm(ra, rb)
     for dt in (torch.float32, torch.bfloat16):
         c = nv.nvfp4_gemm(qa, qb, dt)
         assert_gemm_close(c.float().cpu().numpy(), C, S, dt == torch.bfloat16, f"tiny {dt}")
+    q_sr = nv.nvfp4_quantize(a.cuda(), ws, round_mode=nv.SR, seed=W.SR_SEED, stream_id=0)
+    assert_q_equal(q_sr, O.quantize(np32(a), sr=True, seed=W.SR_SEED, stream=0), "tiny A SR")
+    signs = O.rht_signs_from_seed(W.RHT_SEED)
+    y = nv.nvfp4_rht16(a.cuda(), 1, signs)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32),
+                          O.rht16(np32(a), 1, signs).view(np.uint32)), "tiny A RHT16 along K"
+    assert nv.nvfp4_device_status(ws) == nv.OK
 
 
 # K % 128 == 0 with K >= 384 takes the LDS-slab kernel (ragged edge tiles,

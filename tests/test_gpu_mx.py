@@ -84,6 +84,7 @@ def test_gemm_full_fprop_sampled(nv):
     y = nv.nvfp4_gemm(qx, qw, torch.bfloat16)
     rx, rw = O.mx_quantize(x.float().numpy()), O.mx_quantize(w.float().numpy())
     _check_q(qx, rx, "x")
+    _check_q(qw, rw, "w")
     g = np.random.default_rng(9)
     ms, ns = g.integers(0, 8192, 256), g.integers(0, 20480, 256)
     um, im = np.unique(ms, return_inverse=True)

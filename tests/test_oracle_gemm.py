@@ -74,3 +74,19 @@ def test_quantised_gemm_close_to_float_gemm():
     ref = x.astype(np.float64) @ w.astype(np.float64).T
     rel = np.linalg.norm(C - ref) / np.linalg.norm(ref)
     assert rel < 0.15
+
+
+def test_tiny_config_oracle_finishes_within_a_second():
+    """The tiny configuration end to end on the oracle (A 1x16 RN, B 16x16
+    RN, the float64 product, A with stochastic rounding, RHT16 of A along K)
+    takes well under a second."""
+    import time
+
+    import workloads as W
+    a, b = (t.numpy() for t in W.tiny_pair())
+    t0 = time.perf_counter()
+    qa, (qb, _) = O.quantize(a), O.quantize_2d(b, want_t=False)
+    O.gemm(qa, qb)
+    O.quantize(a, sr=True, seed=W.SR_SEED, stream=0)
+    O.rht16(a, 1, O.rht_signs_from_seed(W.RHT_SEED))
+    assert time.perf_counter() - t0 < 1.0

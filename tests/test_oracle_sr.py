@@ -132,3 +132,41 @@ def test_sr_stream_is_uniform():
 def test_rht_signs_from_seed():
     assert O.rht_signs_from_seed(0) == O.philox4x32_10([0, 0, 0, 0], [0, 0])[0] & 0xFFFF
     assert O.rht_signs_from_seed(0) == 0xE8D5  # low half of the first KAT word
+
+
+def test_sr_probability_dense_grid():
+    """[Review s10 SR formula; s4]: P(round up) = (|v| - lo) / (hi - lo).
+    Over a dense grid of magnitudes in every E2M1 interval -- [0, 0.5) down
+    to 2^-40, [0.5, 1) and [1, 1.5) where the 22-bit fraction and the fp32
+    spacing interact, up to [4, 6) -- and the fp32 neighbours of every grid
+    point, the round-up share over all 2^16 draws lies within 2^-16 of that
+    exact probability; at and above 6 the code is always 6."""
+    from fractions import Fraction
+    rng = np.random.default_rng(20250)
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    vals = []
+    for lo, hi in zip(grid[:-1], grid[1:]):
+        vals += list(rng.uniform(lo, hi, 48).astype(np.float32))
+        for p in (lo, hi):
+            f = np.float32(p)
+            vals += [np.nextafter(f, np.float32(0)), f, np.nextafter(f, np.float32(7))]
+    vals += list(np.float32(2.0) ** rng.uniform(-40, -1, 48).astype(np.float32))
+    vals = np.unique(np.array([v for v in vals if 0 < v < 6], np.float32))
+    r = np.tile(np.arange(65536, dtype=np.uint32), 1)
+    worst = 0.0
+    for i in range(0, vals.size, 32):
+        chunk = vals[i:i + 32]
+        m = np.repeat(chunk, 65536)
+        idx = O.e2m1_sr_index_n(m, np.tile(r, chunk.size)).reshape(chunk.size, 65536)
+        for v, row in zip(chunk, idx):
+            vf = Fraction(float(v))
+            lo = max(k for k, t in enumerate(grid) if Fraction(t) <= vf)
+            frac = (vf - Fraction(grid[lo])) / (Fraction(grid[lo + 1]) - Fraction(grid[lo]))
+            assert set(np.unique(row)) <= {lo, lo + 1}, v
+            p_up = Fraction(int((row == lo + 1).sum()), 65536)
+            worst = max(worst, abs(float(p_up - frac)))
+            assert abs(p_up - frac) <= Fraction(1, 65536), (float(v), float(p_up), float(frac))
+    assert worst > 0  # the grid does reach the 16-bit resolution limit somewhere
+    for v in (6.0, 6.5, 100.0, 3e38):
+        idx = O.e2m1_sr_index_n(np.full(4096, v, np.float32), np.arange(4096, dtype=np.uint32) * 16)
+        assert np.all(idx == 7)
