@@ -125,8 +125,10 @@ __device__ __forceinline__ uint32_t fp4x2_rn(uint32_t old, float a, float b) {
 }
 
 // Eight values -> eight nearest-even codes in one dword (value i in nibble i).
+// The four converts write all four bytes, so the register the chain starts
+// from (v[0]'s, already live) needs no clearing.
 __device__ __forceinline__ uint32_t fp4x8_rn(const float* v) {
-  uint32_t w = 0;
+  uint32_t w = __float_as_uint(v[0]);
   w = fp4x2_rn<0>(w, v[0], v[1]);
   w = fp4x2_rn<1>(w, v[2], v[3]);
   w = fp4x2_rn<2>(w, v[4], v[5]);
@@ -179,6 +181,33 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c
   return U4{c0, c1, c2, c3};
 }
 
+// Philox4x32-10 with output words 0 and 2 complemented: the last round's
+// three-input xor for those words becomes an xnor at no cost (truth table
+// 0x69), for callers that want ~word anyway.
+__device__ __forceinline__ U4 philox4x32_10_n02(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t n0, n2;
+    if (r < 9) {
+      n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+      n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+    } else {
+      n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x69);
+      n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x69);
+    }
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
 // The eight 16-bit draws of elements e .. e+7 (e % 8 == 0) of one operand.
 __device__ __forceinline__ U4 sr_draw8(uint64_t seed, uint32_t stream, uint64_t e) {
   const uint64_t j = e >> 3;
@@ -195,6 +224,99 @@ __device__ __forceinline__ uint32_t fp4x8_sr(const float* v, const U4& r) {
   for (int k = 0; k < 4; ++k)
     out |= fp4x2_sr(v[2 * k], v[2 * k + 1], w[k] & 0xFFFFu, w[k] >> 16) << (8 * k);
   return out;
+}
+
+// ---------------------------------------------------------------- block scales (fast path)
+
+// E4M3 code of a block's t = amax_b * s_enc/6 (non-negative, finite): gfx950's
+// fp8 convert rounds to nearest-even over the E4M3FN grid, subnormals
+// included, but turns values past the largest finite one into NaN, so t is
+// first clamped at 448; the pair (t, 0) packs code | 0 << 8 into the low word
+// (an on-GPU sweep over 281k values of t, every midpoint of the grid and its
+// fp32 neighbours, matched the rounding rule of e4m3_encode exactly).
+__device__ __forceinline__ uint32_t e4m3_code(float t) {
+  const float c = __builtin_fminf(t, 448.0f);
+  // the upper word is left as it was in the destination (unused, masked off)
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, (int)__float_as_uint(c), false) & 0xFFu;
+}
+
+// Value of E4M3FN code c (0..126): subnormal m * 2^-9, normal (1 + m/8) 2^(e-7).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// ---------------------------------------------------------------- packed bf16 elements
+
+// Element j (0..7) of a row of 8 bf16 held in 4 dwords, as fp32.
+__device__ __forceinline__ float bf16_elem(const uint32_t* w, int j) {
+  return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+}
+// The same with its sign bit flipped when sm == 0x80000000 (sm is 0 or
+// that): (w << 16) + sm for the low half, (w & 0xFFFF0000) ^ sm for the high.
+__device__ __forceinline__ float bf16_elem_signed(const uint32_t* w, int j, uint32_t sm) {
+  const uint32_t x = w[j >> 1];
+  return (j & 1) ? __uint_as_float(__builtin_amdgcn_bitop3_b32(x, 0xFFFF0000u, sm, 0x6A))
+                 : __uint_as_float((x << 16) + sm);
+}
+
+// ---------------------------------------------------------------- stochastic E2M1 (pairs)
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// One stochastic FP4 convert of the pair p into byte SEL of `old`, the other
+// bytes kept (the instruction writes only the selected byte; the builtin does
+// not model that, so it is written out with the destination tied).  The
+// trailing s_nop is the one wait state a VALU read of the result needs.
+// SEL < 0: byte 0 of a fresh register (the other bytes are left undefined;
+// the caller fills them with SEL 1..3).
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_sr_byte(uint32_t old, float2_t p, uint32_t rnd) {
+  if (SEL < 0)
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0\n\ts_nop 0" : "=v"(old) : "v"(p), "v"(rnd));
+  else if (SEL == 0)
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0\n\ts_nop 0" : "+v"(old) : "v"(p), "v"(rnd));
+  else if (SEL == 1)
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]\n\ts_nop 0"
+                 : "+v"(old) : "v"(p), "v"(rnd));
+  else if (SEL == 2)
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]\n\ts_nop 0"
+                 : "+v"(old) : "v"(p), "v"(rnd));
+  else
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]\n\ts_nop 0"
+                 : "+v"(old) : "v"(p), "v"(rnd));
+  return old;
+}
+
+// The eight draws of elements e .. e+7 as sr_draw8, with words 0 and 2
+// complemented (see philox4x32_10_n02).
+__device__ __forceinline__ U4 sr_draw8_n02(uint64_t seed, uint32_t stream, uint64_t e) {
+  const uint64_t j = e >> 3;
+  return philox4x32_10_n02((uint32_t)j, (uint32_t)(j >> 32), stream, 0u, (uint32_t)seed,
+                           (uint32_t)(seed >> 32));
+}
+
+// Eight values -> eight SR codes (value i in nibble i) from the four words of
+// one Philox output as sr_draw8_n02 returns it (value 2k takes the low half of
+// word k, value 2k+1 the high half), by the rule of fp4x2_sr.  Each pair is
+// converted twice with the same operands: once with the even value's draw
+// placed for slot 0 (its code lands in the low nibble of byte k of E) and once
+// with the odd value's draw placed for slot 1 (high nibble of byte k of O);
+// nw = ~word gives both fields: slot 0 reads bits 31..10 = ~lo16 then ones,
+// slot 1 bits 30..9 = ~hi16 then ones.
+__device__ __forceinline__ uint32_t fp4x8_sr2(const float* v, const U4& r) {
+  const uint32_t nws[4] = {r.x, ~r.y, r.z, ~r.w};  // words 0 and 2 arrive complemented
+  uint32_t E, O;
+#define NVFP4_SR_PAIR(K, SEL)                                         \
+  {                                                                   \
+    const float2_t p = {v[2 * K], v[2 * K + 1]};                      \
+    const uint32_t nw = nws[K];                                       \
+    E = cvt_sr_byte<SEL>(E, p, (nw << 16) | 0xFFFFu);                 \
+    O = cvt_sr_byte<SEL>(O, p, (nw >> 1) | 0x7E00u);                  \
+  }
+  NVFP4_SR_PAIR(0, -1) NVFP4_SR_PAIR(1, 1) NVFP4_SR_PAIR(2, 2) NVFP4_SR_PAIR(3, 3)
+#undef NVFP4_SR_PAIR
+  return (E & 0x0F0F0F0Fu) | (O & 0xF0F0F0F0u);
 }
 
 // ---------------------------------------------------------------- RHT16

@@ -207,9 +207,10 @@ hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int
 // Reads one copy's amax word; flags the status word and returns false when
 // the amax is not finite (that copy is then skipped).
 __device__ __forceinline__ bool copy_scales(const uint32_t* amax, uint32_t* status,
-                                            TensorScales* ts) {
+                                            TensorScales* ts, uint32_t* amax_bits = nullptr) {
   const int lane = threadIdx.x & 63;
   const uint32_t bits = wave_max_u32(lane < kAmaxSlots ? amax[lane * kAmaxStride] : 0u);
+  if (amax_bits) *amax_bits = bits;
   if (bits >= kInfBits) {
     if (threadIdx.x == 0) atomicMax(status, kStatusNonfinite);
     return false;
@@ -244,11 +245,118 @@ __device__ __forceinline__ bool emit_tile(int64_t rows, int64_t cols, int64_t* t
   return true;
 }
 
+// One thread's 16 x 8 source patch kept as loaded: bf16 pairs (4 dwords a
+// row) or fp32 (8 dwords a row).  Loads as in load_patch (rows past the tile
+// read as zeros through the buffer's record count; a column group past
+// `cols` is zeroed).
+template <typename TIn>
+struct RawPatch {
+  static constexpr int kW = 2 * sizeof(TIn);
+  uint32_t w[16][kW];
+};
+
+template <typename TIn>
+__device__ __forceinline__ void load_raw(const TIn* x, int64_t tile_r0, int64_t tile_rows,
+                                         int64_t cols, int64_t ld, int prow, int64_t c0,
+                                         RawPatch<TIn>& p) {
+  constexpr uint32_t kEs = sizeof(TIn);
+  const uint32_t stride = (uint32_t)ld * kEs;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<TIn*>(x + tile_r0 * ld), (short)0, (int)((uint32_t)tile_rows * stride),
+      0x00020000);
+  const bool col_ok = c0 < cols;
+  const uint32_t voff = col_ok ? (uint32_t)prow * stride + (uint32_t)c0 * kEs : 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int q = 0; q < RawPatch<TIn>::kW / 4; ++q) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16u * q, (uint32_t)i * stride, 0);
+      p.w[i][4 * q + 0] = w[0];
+      p.w[i][4 * q + 1] = w[1];
+      p.w[i][4 * q + 2] = w[2];
+      p.w[i][4 * q + 3] = w[3];
+    }
+  }
+  if (!col_ok) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int q = 0; q < RawPatch<TIn>::kW; ++q) p.w[i][q] = 0u;
+  }
+}
+
+// Element (i, j) of the patch as fp32, and the same with its sign bit flipped
+// when sm == 0x80000000 (the RHT sign diagonal, applied on the way in).
+__device__ __forceinline__ float patch_elem(const RawPatch<uint16_t>& p, int i, int j) {
+  return bf16_elem(p.w[i], j);
+}
+__device__ __forceinline__ float patch_elem(const RawPatch<float>& p, int i, int j) {
+  return __uint_as_float(p.w[i][j]);
+}
+__device__ __forceinline__ float patch_elem_s(const RawPatch<uint16_t>& p, int i, int j,
+                                              uint32_t sm) {
+  return bf16_elem_signed(p.w[i], j, sm);
+}
+__device__ __forceinline__ float patch_elem_s(const RawPatch<float>& p, int i, int j, uint32_t sm) {
+  return __uint_as_float(p.w[i][j] ^ sm);
+}
+
+// Butterflies of the 16-point transform on u[0..15] (signs already applied):
+// h = 1, 2, 4, 8 as (a+b, a-b) [Review s3]; the final x 1/4 is the caller's.
+__device__ __forceinline__ void fwht16(float* u) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = u[i], b = u[i + h];
+      u[i] = a + b;
+      u[i + h] = a - b;
+    }
+  }
+}
+// Four 4-point transforms on u[0..3], u[4..7], ... (signs applied): h = 1, 2
+// [Captions Fig. 12]; the final x 1/2 is the caller's.
+__device__ __forceinline__ void fwht4x4(float* u) {
+#pragma unroll
+  for (int c = 0; c < 16; c += 4) {
+#pragma unroll
+    for (int h = 1; h < 4; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i & h) continue;
+        const float a = u[c + i], b = u[c + i + h];
+        u[c + i] = a + b;
+        u[c + i + h] = a - b;
+      }
+    }
+  }
+}
+
+typedef __amdgpu_buffer_rsrc_t out_rsrc_t;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Raw buffer over an output region starting at `base` (stores take a per-lane
+// offset and a scalar one; validity is decided by the caller's lane mask).
+__device__ __forceinline__ out_rsrc_t out_rsrc(void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, -1, 0x00020000);
+}
+
+// Element multipliers r = s_enc / d for every E4M3 code d (0 for d = 0,
+// saturated at FLT_MAX), times the power of two m (1, or the transform's
+// 1/4 or 1/2 when that is folded in; exact there, see the column copy), so
+// that a block's multiplier is one LDS read of its scale code instead of a
+// division.
+__device__ __forceinline__ void fill_rtab(float* tab, float s_enc, int c, float m = 1.0f) {
+  tab[c] = elem_multiplier(s_enc, e4m3_value((uint32_t)c)) * m;
+}
+
 template <typename TIn, int F>
 __global__ __launch_bounds__(2 * emit_rows(F)) void quant_tile_kernel(TileArgs a) {
   constexpr int TR = emit_rows(F);
   constexpr bool ROW = F & kFRow, COL = F & kFCol, TWO_D = F & kF2D, RHT = F & kFRht;
   constexpr bool SR_ROW = F & kFSrRow, SR_COL = F & kFSrCol, RHT4 = F & kFRht4;
+  __shared__ float rtab[2][128];
 
   const int t = threadIdx.x, cg = t & 31, rs = t >> 5;
   const int64_t rows = a.rows, cols = a.cols;
@@ -259,122 +367,170 @@ __global__ __launch_bounds__(2 * emit_rows(F)) void quant_tile_kernel(TileArgs a
 
   TensorScales tr{}, tc{};
   bool do_row = false, do_col = false;
+  uint32_t col_amax = 0;
   if (ROW) do_row = copy_scales(a.row.amax, a.status, &tr);
   if (COL) {
     if (TWO_D && ROW) {
       do_col = do_row;
       tc = tr;
     } else {
-      do_col = copy_scales(a.col.amax, a.status, &tc);
+      do_col = copy_scales(a.col.amax, a.status, &tc, &col_amax);
     }
   }
+  // Folding the transform's final 1/4 (1/2 for d = 4) into the multiplier.
+  // For bf16 sources every butterfly result u' is exact on the 2^-133 grid or
+  // rounded in the normal range, so u = u' * 1/4 is exact, the block amax is
+  // (max |u'|) * 1/4 exactly, and v = u * r = u' * (r/4) is the same real
+  // product under one rounding -- provided r/4 is exact, which holds while
+  // the operand's amax stays below 2^100 (r >= s_enc / 448 > 2^-98).
+  constexpr bool kCanFold = (RHT || RHT4) && sizeof(TIn) == 2;
+  constexpr float kHs = RHT4 ? 0.5f : 0.25f;
+  const bool fold = kCanFold && col_amax < 0x71800000u;  // 2^100; uniform
   if (blockIdx.x == 0 && t == 0) {
     if (do_row) *a.row.global = tr.g;
     if (do_col && a.col.global) *a.col.global = tc.g;
   }
   if (!do_row && !do_col) return;  // uniform across the workgroup
+  // multiplier tables: [0] row copy (or the 16x16 copies), [1] column copy
+  if (t < 128) {
+    if (ROW && do_row) fill_rtab(rtab[0], tr.s_enc, t);
+    else if (TWO_D && do_col) fill_rtab(rtab[0], tc.s_enc, t);
+  } else if (t < 256 && COL && !TWO_D && do_col) {
+    fill_rtab(rtab[1], tc.s_enc, t - 128, fold ? kHs : 1.0f);
+  }
+  __syncthreads();
 
-  float v[16][8];
-  load_patch(static_cast<const TIn*>(a.x), tile_r0, min(rows - tile_r0, (int64_t)TR), cols,
-             a.ld, rs * 16, c0, v);
+  RawPatch<TIn> p;
+  load_raw(static_cast<const TIn*>(a.x), tile_r0, min(rows - tile_r0, (int64_t)TR), cols, a.ld,
+           rs * 16, c0, p);
 
   if (TWO_D) {
     // ---- one scale per 16x16 tile [Review s2]: this patch and lane ^ 1's
+    const TensorScales& ts = ROW ? tr : tc;
+    float v[16][8];
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) am = fmaxf(am, __builtin_fabsf(v[i][j]));
+      for (int j = 0; j < 8; ++j) {
+        v[i][j] = patch_elem(p, i, j);
+        am = fmaxf(am, __builtin_fabsf(v[i][j]));
+      }
     am = fmaxf(am, lane_xor1(am));
-    uint32_t dcode;
-    // without the row copy (W^T only) the tensor scales come from the column slot
-    const float r = block_scale(am, ROW ? tr : tc, &dcode);
+    const uint32_t dcode = e4m3_code(am * ts.s6);
+    const float r = rtab[0][dcode];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = v[i][j] * r;
     if (valid) {
       const int64_t gcols = cols / 16, grows = rows / 16;
       if (ROW) {
+        const out_rsrc_t oc = out_rsrc(a.row.codes + tile_r0 * (cols / 2) + tile_c0 / 2);
+        const uint32_t vo = (uint32_t)(rs * 16 * (cols / 2) + cg * 4);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float s[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) s[j] = v[i][j] * r;
-          *reinterpret_cast<uint32_t*>(a.row.codes + (r0 + i) * (cols / 2) + c0 / 2) =
-              fp4x8_rn(s);
-        }
+        for (int i = 0; i < 16; ++i)
+          __builtin_amdgcn_raw_buffer_store_b32(fp4x8_rn(v[i]), oc, vo, (uint32_t)(i * (cols / 2)), 0);
       }
       if ((cg & 1) == 0) {
         if (ROW) a.row.scales[(r0 / 16) * gcols + c0 / 16] = (uint8_t)dcode;
         if (COL) a.col.scales[(c0 / 16) * grows + r0 / 16] = (uint8_t)dcode;
       }
       if (COL) {
+        const out_rsrc_t oc = out_rsrc(a.col.codes + tile_c0 * (rows / 2) + tile_r0 / 2);
+        const uint32_t vo = (uint32_t)(cg * 8 * (rows / 2) + rs * 8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           float s[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[i] = v[i][j] * r;
-          uint2 w;
-          w.x = fp4x8_rn(s);
-          w.y = fp4x8_rn(s + 8);
-          *reinterpret_cast<uint2*>(a.col.codes + (c0 + j) * (rows / 2) + r0 / 2) = w;
+          for (int i = 0; i < 16; ++i) s[i] = v[i][j];
+          const u32x2_t w = {fp4x8_rn(s), fp4x8_rn(s + 8)};
+          __builtin_amdgcn_raw_buffer_store_b64(w, oc, vo, (uint32_t)(j * (rows / 2)), 0);
         }
       }
     }
   } else {
     // ---- row-wise copy: 1x16 blocks along cols [Review s1 Steps 2-3]
     if (ROW && do_row) {
+      const out_rsrc_t oc = out_rsrc(a.row.codes + tile_r0 * (cols / 2) + tile_c0 / 2);
+      const out_rsrc_t os = out_rsrc(a.row.scales + tile_r0 * (cols / 16) + tile_c0 / 16);
+      const uint32_t vo = (uint32_t)(rs * 16 * (cols / 2) + cg * 4);
+      const uint32_t vs = (uint32_t)(rs * 16 * (cols / 16) + (cg >> 1));
+      const uint64_t e0 = a.row.offset + (uint64_t)(r0 * cols + c0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        float x[8];
         float am = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) am = fmaxf(am, __builtin_fabsf(v[i][j]));
+        for (int j = 0; j < 8; ++j) {
+          x[j] = patch_elem(p, i, j);
+          am = fmaxf(am, __builtin_fabsf(x[j]));
+        }
         am = fmaxf(am, lane_xor1(am));
-        uint32_t dcode;
-        const float r = block_scale(am, tr, &dcode);
-        if (valid && r0 + i < rows) {
-          float s[8];
+        const uint32_t dcode = e4m3_code(am * tr.s6);
+        const float r = rtab[0][dcode];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) s[j] = v[i][j] * r;
-          uint32_t w;
-          if (SR_ROW)
-            w = fp4x8_sr(s, sr_draw8(a.row.seed, a.row.stream,
-                                     a.row.offset + (uint64_t)((r0 + i) * cols + c0)));
-          else
-            w = fp4x8_rn(s);
-          *reinterpret_cast<uint32_t*>(a.row.codes + (r0 + i) * (cols / 2) + c0 / 2) = w;
-          if ((cg & 1) == 0) a.row.scales[(r0 + i) * (cols / 16) + c0 / 16] = (uint8_t)dcode;
+        for (int j = 0; j < 8; ++j) x[j] = x[j] * r;
+        uint32_t w;
+        if (SR_ROW)
+          w = fp4x8_sr2(x, sr_draw8_n02(a.row.seed, a.row.stream, e0 + (uint64_t)(i * cols)));
+        else
+          w = fp4x8_rn(x);
+        if (valid && r0 + i < rows) {
+          __builtin_amdgcn_raw_buffer_store_b32(w, oc, vo, (uint32_t)(i * (cols / 2)), 0);
+          if ((cg & 1) == 0)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)dcode, os, vs, (uint32_t)(i * (cols / 16)), 0);
         }
       }
     }
     // ---- column-wise copy: 1x16 blocks along rows, optional RHT [Review s3]
     if (COL && do_col) {
+      const out_rsrc_t oc = out_rsrc(a.col.codes + tile_c0 * (rows / 2) + tile_r0 / 2);
+      const out_rsrc_t os = out_rsrc(a.col.scales + tile_c0 * (rows / 16) + tile_r0 / 16);
+      const uint32_t vo = (uint32_t)(cg * 8 * (rows / 2) + rs * 8);
+      const uint32_t vs = (uint32_t)(cg * 8 * (rows / 16) + rs);
+      const uint64_t e0 = a.col.offset + (uint64_t)(c0 * rows + r0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (RHT) rht16_inplace<8>(&v[0][j], a.signs);
-        if (RHT4) rht4_inplace<8>(&v[0][j], a.signs);
+        float u[16];
+        if (RHT || RHT4) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            u[i] = patch_elem_s(p, i, j, ((a.signs >> (RHT4 ? (i & 3) : i)) & 1u) << 31);
+          if (RHT) fwht16(u);
+          else fwht4x4(u);
+          if (!fold) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) u[i] = u[i] * kHs;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) u[i] = patch_elem(p, i, j);
+        }
         float am = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) am = fmaxf(am, __builtin_fabsf(v[i][j]));
-        uint32_t dcode;
-        const float r = block_scale(am, tc, &dcode);
-        float s[16];
+        for (int i = 0; i < 16; ++i) am = fmaxf(am, __builtin_fabsf(u[i]));
+        if (fold) am = am * kHs;
+        const uint32_t dcode = e4m3_code(am * tc.s6);
+        const float r = rtab[1][dcode];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = v[i][j] * r;
-        uint2 w;
+        for (int i = 0; i < 16; ++i) u[i] = u[i] * r;
+        u32x2_t w;
         if (SR_COL) {
-          const uint64_t e = a.col.offset + (uint64_t)((c0 + j) * rows + r0);
-          w.x = fp4x8_sr(s, sr_draw8(a.col.seed, a.col.stream, e));
-          w.y = fp4x8_sr(s + 8, sr_draw8(a.col.seed, a.col.stream, e + 8));
+          const uint64_t e = e0 + (uint64_t)(j * rows);
+          w[0] = fp4x8_sr2(u, sr_draw8_n02(a.col.seed, a.col.stream, e));
+          w[1] = fp4x8_sr2(u + 8, sr_draw8_n02(a.col.seed, a.col.stream, e + 8));
         } else {
-          w.x = fp4x8_rn(s);
-          w.y = fp4x8_rn(s + 8);
+          w[0] = fp4x8_rn(u);
+          w[1] = fp4x8_rn(u + 8);
         }
         if (valid) {
-          *reinterpret_cast<uint2*>(a.col.codes + (c0 + j) * (rows / 2) + r0 / 2) = w;
-          a.col.scales[(c0 + j) * (rows / 16) + r0 / 16] = (uint8_t)dcode;
+          __builtin_amdgcn_raw_buffer_store_b64(w, oc, vo, (uint32_t)(j * (rows / 2)), 0);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)dcode, os, vs, (uint32_t)(j * (rows / 16)), 0);
         }
       }
     }
   }
-
 }
 
 template <typename TIn, int F>

@@ -193,3 +193,30 @@ def test_full_size_w_2d(nv, ws):
     ref, ref_t = O.quantize_2d(np32(w))
     assert_q_equal(q, ref, "W")
     assert_q_equal(qt, ref_t, "W^T")
+
+
+@pytest.mark.parametrize("scale_log2", [-140, -126, -100, 0, 90, 93, 96, 99, 110])
+@pytest.mark.parametrize("sr", [False, True])
+@pytest.mark.parametrize("d", [16, 4])
+def test_col_rht_across_magnitudes(nv, ws, scale_log2, sr, d):
+    """Column copies with the RHT of bf16 data scaled by 2^k across the whole
+    range: tiny values whose transform lands in fp32's subnormal range, and
+    huge ones around the 2^100 amax below which the kernel folds the
+    transform's final 1/4 (or 1/2) into the multiplier.  Codes, scales and
+    tensor scale must equal the oracle's (separate transform, then
+    quantisation) in every case."""
+    x = (_rand(256, 384, torch.float32, 40 + scale_log2 & 0xFF, p=0.02, mul=20.0) *
+         2.0 ** scale_log2).to(torch.bfloat16)
+    x[3, :16] = 0.0
+    x[9, 5] = -0.0
+    xr = np32(x)
+    say("col rht magnitudes", scale_log2, sr, d)
+    q = nv.nvfp4_quantize(x.cuda(), ws, transpose=True, rht=True, rht_d=d, rht_signs=SIGNS,
+                          round_mode=nv.SR if sr else nv.RN, seed=77, stream_id=1)
+    if d == 16:
+        ref = O.quantize(xr, transpose=True, rht=True, signs=SIGNS, sr=sr, seed=77, stream=1)
+    else:
+        sg = [SIGNS & 0xF, 0, 0, 0]
+        ref = O.quantize(O.rht(xr, 0, 4, sg), transpose=True, sr=sr, seed=77, stream=1)
+    assert nv.nvfp4_device_status(ws) == nv.OK
+    assert_q_equal(q, ref, f"col rht d={d} 2^{scale_log2}")
