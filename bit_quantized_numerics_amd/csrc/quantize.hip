@@ -35,7 +35,8 @@ namespace nvfp4 {
 constexpr int kTileR = 256;  // source rows per workgroup
 constexpr int kTileC = 256;  // source cols per workgroup
 constexpr int kThreads = 512;
-constexpr int kStatsTileR = 128;  // stats kernel: 128 rows x 256 cols, 256 threads
+constexpr int kStatsRows = 64;    // stats kernel: 64 rows x 512 cols, 256 threads
+constexpr int kStatsCols = 512;
 constexpr int kStatsThreads = 256;
 
 // ---------------------------------------------------------------- zero
@@ -103,148 +104,6 @@ __device__ __forceinline__ void load_patch(const TIn* x, int64_t tile_r0, int64_
   }
 }
 
-// ---------------------------------------------------------------- stats
-// Tensor amax [Review s1 Step 1] as the largest |x| bit pattern (Inf/NaN sort
-// above every finite value, so a non-finite input is never lost), and with
-// RHTC also the amax of the transform along rows (the Wgrad copies take their
-// scale after the transform): RD = 16, or RD = 4 (four 4-point transforms per
-// 16-row patch column, the Hadamard-size ablation).
-
-template <typename TIn, bool RAW, bool RHTC, int RD = 16>
-__global__ __launch_bounds__(kStatsThreads) void amax_kernel(const TIn* __restrict__ x,
-                                                             int64_t rows, int64_t cols, int64_t ld,
-                                                             uint32_t signs, uint32_t* out_raw,
-                                                             uint32_t* out_rht) {
-  const int t = threadIdx.x, cg = t & 31, rs = t >> 5;
-  const int64_t r0 = (int64_t)blockIdx.y * kStatsTileR + rs * 16;
-  const int64_t c0 = (int64_t)blockIdx.x * kTileC + cg * 8;
-  const int64_t tile_r0 = (int64_t)blockIdx.y * kStatsTileR;
-  float v[16][8];
-  load_patch(x, tile_r0, min(rows - tile_r0, (int64_t)kStatsTileR), cols, ld, rs * 16, c0, v);
-  (void)r0;
-  uint32_t m_raw = 0, m_rht = 0;
-  if (RAW) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t b = __float_as_uint(v[i][j]) & 0x7FFFFFFFu;
-        m_raw = m_raw > b ? m_raw : b;
-      }
-  }
-  if (RHTC) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (RD == 4)
-        rht4_inplace<8>(&v[0][j], signs);
-      else
-        rht16_inplace<8>(&v[0][j], signs);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t b = __float_as_uint(v[i][j]) & 0x7FFFFFFFu;
-        m_rht = m_rht > b ? m_rht : b;
-      }
-  }
-  __shared__ uint32_t red[2][kStatsThreads / 64];
-  if (RAW) m_raw = wave_max_u32(m_raw);
-  if (RHTC) m_rht = wave_max_u32(m_rht);
-  if ((t & 63) == 0) {
-    red[0][t >> 6] = m_raw;
-    red[1][t >> 6] = m_rht;
-  }
-  __syncthreads();
-  if (t == 0) {
-    uint32_t r0 = 0, r1 = 0;
-#pragma unroll
-    for (int w = 0; w < kStatsThreads / 64; ++w) {
-      r0 = r0 > red[0][w] ? r0 : red[0][w];
-      r1 = r1 > red[1][w] ? r1 : red[1][w];
-    }
-    const int slot = (int)((blockIdx.x + blockIdx.y * 7u) % kAmaxSlots) * kAmaxStride;
-    if (RAW) atomicMax(out_raw + slot, r0);
-    if (RHTC) atomicMax(out_rht + slot, r1);
-  }
-}
-
-template <typename TIn>
-static hipError_t amax_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ld,
-                                uint32_t signs, uint32_t* out_raw, uint32_t* out_rht,
-                                hipStream_t s, int rht_d) {
-  const dim3 grid((unsigned)((cols + kTileC - 1) / kTileC),
-                  (unsigned)((rows + kStatsTileR - 1) / kStatsTileR));
-  const TIn* p = static_cast<const TIn*>(x);
-  if (rht_d == 4) {
-    if (out_raw || !out_rht) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((amax_kernel<TIn, false, true, 4>), grid, dim3(kStatsThreads), 0, s, p, rows,
-                       cols, ld, signs, out_raw, out_rht);
-    return hipGetLastError();
-  }
-  if (out_raw && out_rht)
-    hipLaunchKernelGGL((amax_kernel<TIn, true, true>), grid, dim3(kStatsThreads), 0, s, p, rows, cols,
-                       ld, signs, out_raw, out_rht);
-  else if (out_raw)
-    hipLaunchKernelGGL((amax_kernel<TIn, true, false>), grid, dim3(kStatsThreads), 0, s, p, rows,
-                       cols, ld, signs, out_raw, out_rht);
-  else
-    hipLaunchKernelGGL((amax_kernel<TIn, false, true>), grid, dim3(kStatsThreads), 0, s, p, rows,
-                       cols, ld, signs, out_raw, out_rht);
-  return hipGetLastError();
-}
-
-hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
-                       uint32_t signs, uint32_t* out_raw, uint32_t* out_rht, hipStream_t s,
-                       int rht_d) {
-  if (dtype == kDtypeBF16)
-    return amax_dispatch<uint16_t>(x, rows, cols, ld, signs, out_raw, out_rht, s, rht_d);
-  return amax_dispatch<float>(x, rows, cols, ld, signs, out_raw, out_rht, s, rht_d);
-}
-
-// ---------------------------------------------------------------- emit
-
-// Reads one copy's amax word; flags the status word and returns false when
-// the amax is not finite (that copy is then skipped).
-__device__ __forceinline__ bool copy_scales(const uint32_t* amax, uint32_t* status,
-                                            TensorScales* ts, uint32_t* amax_bits = nullptr) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t bits = wave_max_u32(lane < kAmaxSlots ? amax[lane * kAmaxStride] : 0u);
-  if (amax_bits) *amax_bits = bits;
-  if (bits >= kInfBits) {
-    if (threadIdx.x == 0) atomicMax(status, kStatusNonfinite);
-    return false;
-  }
-  *ts = tensor_scales(bits);
-  return true;
-}
-
-// Emit tile rows per flag set: 128 (256 threads), or 256 (512 threads) for
-// the 16x16 weight copies.  The smaller tile gives the activation and
-// gradient tensors several workgroups per CU; the weight kernel does little
-// arithmetic per byte, and there the per-workgroup set-up of the larger
-// tile's half as many workgroups measured faster.
-constexpr int emit_rows(int F) { return (F & kF2D) ? 256 : 128; }
-
-// Workgroup -> emit tile.  With 128-row tiles, the two tiles of a 256-row
-// pair write the two halves of every 128-byte line of the column-wise copy,
-// so they are given workgroups b and b + 8: workgroups go round-robin over
-// the 8 XCDs, so both run on the same XCD, one after the other, and its L2
-// merges the halves before the line is written back.  Pair p (column tile
-// fastest) is taken by workgroups 16 (p / 8) + p % 8 and that + 8.  Returns
-// false for the workgroups past the last tile (the grid is rounded up to 16).
-template <int TR>
-__device__ __forceinline__ bool emit_tile(int64_t rows, int64_t cols, int64_t* tile_r0,
-                                          int64_t* tile_c0) {
-  const int64_t gx = (cols + kTileC - 1) / kTileC, gy = (rows + TR - 1) / TR;
-  const int64_t b = blockIdx.x, p = (b >> 4) * 8 + (b & 7);
-  const int64_t ty = 2 * (p / gx) + ((b >> 3) & 1), tx = p % gx;
-  if (ty >= gy) return false;
-  *tile_r0 = ty * TR;
-  *tile_c0 = tx * kTileC;
-  return true;
-}
-
 // One thread's 16 x 8 source patch kept as loaded: bf16 pairs (4 dwords a
 // row) or fp32 (8 dwords a row).  Loads as in load_patch (rows past the tile
 // read as zeros through the buffer's record count; a column group past
@@ -255,7 +114,11 @@ struct RawPatch {
   uint32_t w[16][kW];
 };
 
-template <typename TIn>
+// ZERO: zero a column group past `cols` (the emit kernels); without it that
+// lane re-reads columns 0..7 of the tile's first 16 rows, which leaves a
+// maximum unchanged (the stats kernel, where a conditional overwrite of
+// registers with loads in flight would make the compiler wait for them).
+template <typename TIn, bool ZERO = true>
 __device__ __forceinline__ void load_raw(const TIn* x, int64_t tile_r0, int64_t tile_rows,
                                          int64_t cols, int64_t ld, int prow, int64_t c0,
                                          RawPatch<TIn>& p) {
@@ -277,7 +140,7 @@ __device__ __forceinline__ void load_raw(const TIn* x, int64_t tile_r0, int64_t 
       p.w[i][4 * q + 3] = w[3];
     }
   }
-  if (!col_ok) {
+  if (ZERO && !col_ok) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
@@ -333,6 +196,178 @@ __device__ __forceinline__ void fwht4x4(float* u) {
   }
 }
 
+// |x| maximum of the patch as an fp32 bit pattern (Inf/NaN sort above every
+// finite value): packed 16-bit integer maxima of the bf16 magnitudes.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t patch_absmax_bits(const RawPatch<uint16_t>& p) {
+  u16x2_t m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, p.w[i][q] & 0x7FFF7FFFu));
+  const uint32_t lo = m[0], hi = m[1];
+  return (lo > hi ? lo : hi) << 16;
+}
+__device__ __forceinline__ uint32_t patch_absmax_bits(const RawPatch<float>& p) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t b = p.w[i][q] & 0x7FFFFFFFu;
+      m = m > b ? m : b;
+    }
+  return m;
+}
+
+// ---------------------------------------------------------------- stats
+// Tensor amax [Review s1 Step 1] as the largest |x| bit pattern (Inf/NaN sort
+// above every finite value, so a non-finite input is never lost), and with
+// RHTC also the amax of the transform along rows (the Wgrad copies take their
+// scale after the transform): RD = 16, or RD = 4 (four 4-point transforms per
+// 16-row patch column, the Hadamard-size ablation).  The transform's final
+// 1/4 (1/2) is applied once to the workgroup's maximum instead of to every
+// element: rounding is monotonic, so f32(max |u'| * c) = max f32(|u'| * c).
+//
+// A workgroup reads a 64-row x 512-column tile; each wave takes one 16-row
+// strip, so every load instruction of a wave reads 1 KB of one row (bf16).
+// (A persistent form that walked the tiles with the next tile's loads in
+// flight measured slower inside the layer step.)
+
+template <typename TIn, bool RAW, bool RHTC, int RD = 16>
+__global__ __launch_bounds__(kStatsThreads) void amax_kernel(const TIn* __restrict__ x,
+                                                             int64_t rows, int64_t cols, int64_t ld,
+                                                             uint32_t signs, uint32_t* out_raw,
+                                                             uint32_t* out_rht) {
+  const int t = threadIdx.x, cg = t & 63, rs = t >> 6;
+  const int64_t gx = (cols + kStatsCols - 1) / kStatsCols;
+  const int64_t tile_r0 = ((int64_t)blockIdx.x / gx) * kStatsRows;
+  const int64_t c0 = ((int64_t)blockIdx.x % gx) * kStatsCols + cg * 8;
+  RawPatch<TIn> p;
+  load_raw<TIn, false>(x, tile_r0, min(rows - tile_r0, (int64_t)kStatsRows), cols, ld, rs * 16, c0,
+                       p);
+  uint32_t m_raw = 0, m_rht = 0;
+  if (RAW) m_raw = patch_absmax_bits(p);
+  if (RHTC) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float u[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        u[i] = patch_elem_s(p, i, j, ((signs >> (RD == 4 ? (i & 3) : i)) & 1u) << 31);
+      if (RD == 4) fwht4x4(u);
+      else fwht16(u);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t b = __float_as_uint(u[i]) & 0x7FFFFFFFu;
+        m_rht = m_rht > b ? m_rht : b;
+      }
+    }
+  }
+  __shared__ uint32_t red[2][kStatsThreads / 64];
+  if (RAW) m_raw = wave_max_u32(m_raw);
+  if (RHTC) m_rht = wave_max_u32(m_rht);
+  if ((t & 63) == 0) {
+    red[0][t >> 6] = m_raw;
+    red[1][t >> 6] = m_rht;
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint32_t r0 = 0, r1 = 0;
+#pragma unroll
+    for (int w = 0; w < kStatsThreads / 64; ++w) {
+      r0 = r0 > red[0][w] ? r0 : red[0][w];
+      r1 = r1 > red[1][w] ? r1 : red[1][w];
+    }
+    // the transform's scale, once (Inf and NaN stay at or above kInfBits)
+    if (RHTC && r1 < kInfBits) r1 = __float_as_uint(__uint_as_float(r1) * (RD == 4 ? 0.5f : 0.25f));
+    const int slot = (int)(blockIdx.x % kAmaxSlots) * kAmaxStride;
+    if (RAW) atomicMax(out_raw + slot, r0);
+    if (RHTC) atomicMax(out_rht + slot, r1);
+  }
+}
+
+template <typename TIn>
+static hipError_t amax_dispatch(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                                uint32_t signs, uint32_t* out_raw, uint32_t* out_rht,
+                                hipStream_t s, int rht_d) {
+  const int64_t tiles = ((cols + kStatsCols - 1) / kStatsCols) * ((rows + kStatsRows - 1) / kStatsRows);
+  const dim3 grid((unsigned)tiles);
+  const TIn* p = static_cast<const TIn*>(x);
+  if (rht_d == 4) {
+    if (out_raw || !out_rht) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((amax_kernel<TIn, false, true, 4>), grid, dim3(kStatsThreads), 0, s, p, rows,
+                       cols, ld, signs, out_raw, out_rht);
+    return hipGetLastError();
+  }
+  if (out_raw && out_rht)
+    hipLaunchKernelGGL((amax_kernel<TIn, true, true>), grid, dim3(kStatsThreads), 0, s, p, rows, cols,
+                       ld, signs, out_raw, out_rht);
+  else if (out_raw)
+    hipLaunchKernelGGL((amax_kernel<TIn, true, false>), grid, dim3(kStatsThreads), 0, s, p, rows,
+                       cols, ld, signs, out_raw, out_rht);
+  else
+    hipLaunchKernelGGL((amax_kernel<TIn, false, true>), grid, dim3(kStatsThreads), 0, s, p, rows,
+                       cols, ld, signs, out_raw, out_rht);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       uint32_t signs, uint32_t* out_raw, uint32_t* out_rht, hipStream_t s,
+                       int rht_d) {
+  if (dtype == kDtypeBF16)
+    return amax_dispatch<uint16_t>(x, rows, cols, ld, signs, out_raw, out_rht, s, rht_d);
+  return amax_dispatch<float>(x, rows, cols, ld, signs, out_raw, out_rht, s, rht_d);
+}
+
+// ---------------------------------------------------------------- emit
+
+// Reads one copy's amax word; flags the status word and returns false when
+// the amax is not finite (that copy is then skipped).
+__device__ __forceinline__ bool copy_scales(const uint32_t* amax, uint32_t* status,
+                                            TensorScales* ts, uint32_t* amax_bits = nullptr) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t bits = wave_max_u32(lane < kAmaxSlots ? amax[lane * kAmaxStride] : 0u);
+  if (amax_bits) *amax_bits = bits;
+  if (bits >= kInfBits) {
+    if (threadIdx.x == 0) atomicMax(status, kStatusNonfinite);
+    return false;
+  }
+  *ts = tensor_scales(bits);
+  return true;
+}
+
+// Emit tile rows per flag set: 128 (256 threads), or 256 (512 threads) for
+// the 16x16 weight copies.  The smaller tile gives the activation and
+// gradient tensors several workgroups per CU (64-row tiles measured no faster
+// for X and slower for dY); the weight kernel does little arithmetic per
+// byte, and there the per-workgroup set-up of the larger tile's half as many
+// workgroups measured faster.
+constexpr int emit_rows(int F) { return (F & kF2D) ? 256 : 128; }
+
+// Workgroup -> emit tile.  A 128-byte line of the column-wise copy holds 256
+// tokens, i.e. G = 256 / TR vertically adjacent tiles; those tiles are given
+// workgroups b, b + 8, ..., b + 8 (G - 1): workgroups go round-robin over the
+// 8 XCDs, so all of them run on the same XCD, one after the other, and its L2
+// merges the parts of every line before it is written back.  Line group L
+// (column tile fastest) is taken by the workgroups with (b >> 3) / G == L / 8
+// and b % 8 == L % 8.  Returns false for the workgroups past the last tile
+// (the grid is rounded up to a multiple of 8 G).
+template <int TR>
+__device__ __forceinline__ bool emit_tile(int64_t rows, int64_t cols, int64_t* tile_r0,
+                                          int64_t* tile_c0) {
+  constexpr int G = 256 / TR;
+  const int64_t gx = (cols + kTileC - 1) / kTileC, gy = (rows + TR - 1) / TR;
+  const int64_t b = blockIdx.x, pos = b >> 3;
+  const int64_t L = (pos / G) * 8 + (b & 7);
+  const int64_t ty = (L / gx) * G + pos % G, tx = L % gx;
+  if (ty >= gy) return false;
+  *tile_r0 = ty * TR;
+  *tile_c0 = tx * kTileC;
+  return true;
+}
+
 typedef __amdgpu_buffer_rsrc_t out_rsrc_t;
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -351,8 +386,13 @@ __device__ __forceinline__ void fill_rtab(float* tab, float s_enc, int c, float 
   tab[c] = elem_multiplier(s_enc, e4m3_value((uint32_t)c)) * m;
 }
 
+// At least four waves per SIMD (at most 128 VGPRs) for bf16 sources (an fp32
+// patch alone takes 128 registers): the scheduler otherwise
+// spends registers on overlap within one wave (all 16 rows of a patch in
+// flight) that more resident waves provide better.
 template <typename TIn, int F>
-__global__ __launch_bounds__(2 * emit_rows(F)) void quant_tile_kernel(TileArgs a) {
+__global__ __launch_bounds__(2 * emit_rows(F)) __attribute__((amdgpu_waves_per_eu(sizeof(TIn) == 2 ? 4 : 1)))
+void quant_tile_kernel(TileArgs a) {
   constexpr int TR = emit_rows(F);
   constexpr bool ROW = F & kFRow, COL = F & kFCol, TWO_D = F & kF2D, RHT = F & kFRht;
   constexpr bool SR_ROW = F & kFSrRow, SR_COL = F & kFSrCol, RHT4 = F & kFRht4;
@@ -392,11 +432,13 @@ __global__ __launch_bounds__(2 * emit_rows(F)) void quant_tile_kernel(TileArgs a
   }
   if (!do_row && !do_col) return;  // uniform across the workgroup
   // multiplier tables: [0] row copy (or the 16x16 copies), [1] column copy
-  if (t < 128) {
-    if (ROW && do_row) fill_rtab(rtab[0], tr.s_enc, t);
-    else if (TWO_D && do_col) fill_rtab(rtab[0], tc.s_enc, t);
-  } else if (t < 256 && COL && !TWO_D && do_col) {
-    fill_rtab(rtab[1], tc.s_enc, t - 128, fold ? kHs : 1.0f);
+  for (int c = t; c < 256; c += 2 * TR) {
+    if (c < 128) {
+      if (ROW && do_row) fill_rtab(rtab[0], tr.s_enc, c);
+      else if (TWO_D && do_col) fill_rtab(rtab[0], tc.s_enc, c);
+    } else if (COL && !TWO_D && do_col) {
+      fill_rtab(rtab[1], tc.s_enc, c - 128, fold ? kHs : 1.0f);
+    }
   }
   __syncthreads();
 
@@ -407,44 +449,46 @@ __global__ __launch_bounds__(2 * emit_rows(F)) void quant_tile_kernel(TileArgs a
   if (TWO_D) {
     // ---- one scale per 16x16 tile [Review s2]: this patch and lane ^ 1's
     const TensorScales& ts = ROW ? tr : tc;
-    float v[16][8];
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        v[i][j] = patch_elem(p, i, j);
-        am = fmaxf(am, __builtin_fabsf(v[i][j]));
-      }
+    float am = __uint_as_float(patch_absmax_bits(p));
     am = fmaxf(am, lane_xor1(am));
     const uint32_t dcode = e4m3_code(am * ts.s6);
     const float r = rtab[0][dcode];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = v[i][j] * r;
+    // keep the unpacking below this point: hoisted above the table read it
+    // would hold all 128 values at once (occupancy halves)
+    __builtin_amdgcn_sched_barrier(0);
     if (valid) {
       const int64_t gcols = cols / 16, grows = rows / 16;
       if (ROW) {
         const out_rsrc_t oc = out_rsrc(a.row.codes + tile_r0 * (cols / 2) + tile_c0 / 2);
         const uint32_t vo = (uint32_t)(rs * 16 * (cols / 2) + cg * 4);
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          __builtin_amdgcn_raw_buffer_store_b32(fp4x8_rn(v[i]), oc, vo, (uint32_t)(i * (cols / 2)), 0);
+        for (int i = 0; i < 16; ++i) {
+          float s8[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s8[j] = patch_elem(p, i, j) * r;
+          __builtin_amdgcn_raw_buffer_store_b32(fp4x8_rn(s8), oc, vo, (uint32_t)(i * (cols / 2)), 0);
+        }
       }
       if ((cg & 1) == 0) {
         if (ROW) a.row.scales[(r0 / 16) * gcols + c0 / 16] = (uint8_t)dcode;
         if (COL) a.col.scales[(c0 / 16) * grows + r0 / 16] = (uint8_t)dcode;
       }
       if (COL) {
+        // The same products as the row copy, read down each column.  They are
+        // recomputed from the packed patch rather than kept (128 more
+        // registers): the empty asm hides that r and the zero sign mask
+        // (unpacking through the signed form) repeat the row copy's values.
+        float rc = r;
+        uint32_t z = 0;
+        asm volatile("" : "+v"(rc), "+v"(z));
         const out_rsrc_t oc = out_rsrc(a.col.codes + tile_c0 * (rows / 2) + tile_r0 / 2);
         const uint32_t vo = (uint32_t)(cg * 8 * (rows / 2) + rs * 8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          float s[16];
+          float s16[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[i] = v[i][j];
-          const u32x2_t w = {fp4x8_rn(s), fp4x8_rn(s + 8)};
+          for (int i = 0; i < 16; ++i) s16[i] = patch_elem_s(p, i, j, z) * rc;
+          const u32x2_t w = {fp4x8_rn(s16), fp4x8_rn(s16 + 8)};
           __builtin_amdgcn_raw_buffer_store_b64(w, oc, vo, (uint32_t)(j * (rows / 2)), 0);
         }
       }
@@ -535,10 +579,10 @@ __global__ __launch_bounds__(2 * emit_rows(F)) void quant_tile_kernel(TileArgs a
 
 template <typename TIn, int F>
 static void launch_tile(const TileArgs& a, hipStream_t s) {
-  constexpr int TR = emit_rows(F);
+  constexpr int TR = emit_rows(F), G = 256 / TR;
   const int64_t gx = (a.cols + kTileC - 1) / kTileC, gy = (a.rows + TR - 1) / TR;
-  const int64_t pairs = gx * ((gy + 1) / 2);
-  const dim3 grid((unsigned)(16 * ((pairs + 7) / 8)));
+  const int64_t groups = gx * ((gy + G - 1) / G);
+  const dim3 grid((unsigned)(8 * G * ((groups + 7) / 8)));
   hipLaunchKernelGGL((quant_tile_kernel<TIn, F>), grid, dim3(2 * TR), 0, s, a);
 }
 
