@@ -10,7 +10,11 @@ points nvfp4_linear_fwd and nvfp4_linear_bwd.
 value = 3 * 2 * M * N * K / step time  (TFLOP/s, whole job, one GPU).
 A second timed pass issues the same kernels through the per-operation entry
 points with HIP events between them on the launch stream, giving the
-per-phase times behind `quantize_GBps` and the GEMM roofline.
+per-phase times behind `quantize_GBps` and the GEMM roofline.  A third times
+each step alone between HIP events, with a 512 MB scratch write before it so
+that nothing is left in the memory-side cache, and reports the median of 20
+(`step_ms_event_median_flushed`).  `measured_ceiling` holds what the card
+sustains on a plain 1 GiB device copy and on MFMA-only loops.
 
 Prints ONE JSON line.
 """
@@ -38,6 +42,10 @@ PEAK_FP4_TFLOPS = 10100.0  # MI355X dense fp4 MFMA (the MXFP4 comparator's dtype
 # 1/256 B of 16x16 scales.
 BYTES_ROWCOL = 2.0 + 2 * (0.5 + 1.0 / 16)
 BYTES_2D = 2.0 + 2 * (0.5 + 1.0 / 256)
+# As run: the tensor amax is a pass of its own before the emit pass, so the
+# source is read twice.
+BYTES_ROWCOL_RUN = BYTES_ROWCOL + 2.0
+BYTES_2D_RUN = BYTES_2D + 2.0
 
 # HBM traffic of the GEMM kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (KiB per dispatch; FETCH_SIZE x 2 and WRITE_SIZE x 1, the factors a plain
@@ -242,6 +250,27 @@ def bf16_fprop(nv, x, w, ctx, ws, signs, reps: int):
             "layer_fwd_bf16_fprop_ms": round(tf, 4), "layer_fwd_nvfp4_ms": round(tn, 4)}
 
 
+def hbm_copy_rate(reps: int) -> float:
+    """GB/s of torch's device-to-device copy over 1 GiB (read 1 GiB + write
+    1 GiB per launch), median of `reps` launches timed with HIP events."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    return 2.0 * n * 4 / (ts[len(ts) // 2] * 1e-3) / 1e9
+
+
 def layer_at(nv, W, m: int, signs: int, reps: int):
     """The whole layer step (all quantisations and the three GEMMs, one stream)
     at m tokens: X [m, K], W [N, K], dY [m, N] from the same generators."""
@@ -352,11 +381,39 @@ def main():
     gemm_ms = (ph["gemm_fprop"] + ph["gemm_dgrad"] + ph["gemm_wgrad"]) / 3
     quant_ms = ph["quant_x"] + ph["quant_w"] + ph["quant_dy"]
     qbytes = BYTES_ROWCOL * (M * K + M * N) + BYTES_2D * N * K
+    qbytes_run = BYTES_ROWCOL_RUN * (M * K + M * N) + BYTES_2D_RUN * N * K
     gemm_flops = 2.0 * M * N * K
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
     traffic = None
     if GEMM_TRAFFIC["source_sha1"] == _gemm_source_sha1():
         traffic = GEMM_TRAFFIC["bytes_per_launch"]
+
+    # the same step timed as one HIP-event interval per step on the launch
+    # stream, a 512 MB scratch write between steps so that no operand is
+    # left in the 256 MB memory-side cache, median of 20
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ev_t = []
+    for i in range(20):
+        flush.fill_(i & 0x7F)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ev_t.append(e0.elapsed_time(e1))
+    del flush
+    ev_t.sort()
+    step_median_ms = 0.5 * (ev_t[9] + ev_t[10])
+    copy_gbps = hbm_copy_rate(5)
+
+    def qphase(name, elems, b_alg, b_run):
+        t = ph[name] * 1e-3
+        alg = elems * b_alg / t / 1e9
+        return {"elements": elems, "ms": round(ph[name], 4), "GBps": round(alg, 1),
+                "frac_of_hbm_peak": round(alg / PEAK_HBM_GBPS, 4),
+                "frac_of_measured_copy": round(alg / copy_gbps, 4),
+                "GBps_two_pass_bytes": round(elems * b_run / t / 1e9, 1),
+                "two_pass_frac_of_hbm_peak": round(elems * b_run / t / 1e9 / PEAK_HBM_GBPS, 4)}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -367,8 +424,18 @@ def main():
                                "8192 tokens, 5120->20480",
                    "M": M, "K": K, "N": N, "input_dtype": "bf16", "y_dx_dtype": "bf16",
                    "dw_dtype": "f32", "recipe": "2D W scales, RHT16 on Wgrad inputs, SR on dY"},
+        "step_ms_event_median_flushed": round(step_median_ms, 4),
+        "TFLOPs_event_median_flushed": round(3 * gemm_flops / (step_median_ms * 1e-3) / 1e12, 2),
         "quantize_GBps": round(qbytes / (quant_ms * 1e-3) / 1e9, 1),
         "quantize_frac_of_hbm_peak": round(qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "quantize_frac_of_measured_copy": round(qbytes / (quant_ms * 1e-3) / 1e9 / copy_gbps, 4),
+        "quantize_two_pass_GBps": round(qbytes_run / (quant_ms * 1e-3) / 1e9, 1),
+        "quantize_two_pass_frac_of_hbm_peak": round(qbytes_run / (quant_ms * 1e-3) / 1e9
+                                                    / PEAK_HBM_GBPS, 4),
+        "quantize_phases": {
+            "x_row_and_rht_col": qphase("quant_x", M * K, BYTES_ROWCOL, BYTES_ROWCOL_RUN),
+            "w_16x16_and_transposed": qphase("quant_w", N * K, BYTES_2D, BYTES_2D_RUN),
+            "dy_sr_row_and_sr_rht_col": qphase("quant_dy", M * N, BYTES_ROWCOL, BYTES_ROWCOL_RUN)},
         "phase_ms": {n: round(v, 4) for n, v in ph.items()},
         "roofline": {"bound": "mfma", "kernel": "nvfp4 gemm (f16 MFMA, fp32 acc), avg of 3 launches",
                      "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
@@ -381,20 +448,27 @@ def main():
     # the compute ceiling the card holds under a sustained fp16 MFMA load (no
     # memory traffic), next to the datasheet peak used in `roofline`
     nv.nvfp4_peak_mfma_f16(1000)
+    mfma_pure = nv.nvfp4_peak_mfma_f16(5000, valu_per_mfma=0)
+    mfma_pure_6bit = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0x87E087E0, valu_per_mfma=0)
     mfma_loop = nv.nvfp4_peak_mfma_f16(5000)
     mfma_6bit = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0x87E087E0)
-    mfma_const = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0)
+    mfma_const = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0, valu_per_mfma=0)
     out["measured_ceiling"] = {
-        "mfma_f16_loop_TFLOPs": round(mfma_loop, 1),
-        "mfma_f16_loop_6bit_operands_TFLOPs": round(mfma_6bit, 1),
-        "mfma_f16_loop_constant_operands_TFLOPs": round(mfma_const, 1),
-        "gemm_frac_of_loop": round(achieved / mfma_loop, 4),
-        "gemm_frac_of_6bit_loop": round(achieved / mfma_6bit, 4),
-        "note": "fp16 MFMA-only loop shaped like the GEMM's (16 accumulators per wave, 4 VALU per "
-                "MFMA): operands changing every iteration in sign, one exponent bit and all "
-                "mantissa bits; in sign, that exponent bit and the top 5 mantissa bits (the bit "
-                "pattern of dequantised E2M1 x E4M3 values, at most 6 significant bits); and "
-                "constant operands"}
+        "hbm_copy_GBps": round(copy_gbps, 1),
+        "mfma_f16_pure_TFLOPs": round(mfma_pure, 1),
+        "mfma_f16_pure_6bit_operands_TFLOPs": round(mfma_pure_6bit, 1),
+        "mfma_f16_pure_constant_operands_TFLOPs": round(mfma_const, 1),
+        "mfma_f16_4valu_TFLOPs": round(mfma_loop, 1),
+        "mfma_f16_4valu_6bit_operands_TFLOPs": round(mfma_6bit, 1),
+        "gemm_frac_of_pure": round(achieved / mfma_pure, 4),
+        "gemm_frac_of_pure_6bit": round(achieved / mfma_pure_6bit, 4),
+        "note": "hbm_copy: torch's device copy of 1 GiB (reads and writes 1 GiB), median of 5, "
+                "HIP events. mfma: an fp16 32x32x16 MFMA loop with 16 accumulators per wave and "
+                "one wave per SIMD, as the GEMM runs; 'pure' issues no VALU between MFMAs, "
+                "'4valu' issues 4 independent VALU ops after each; operands alternate between "
+                "two register sets differing in sign, one exponent bit and all mantissa bits, or "
+                "in sign, that exponent bit and the top 5 mantissa bits (the bit pattern of "
+                "dequantised E2M1 x E4M3 values, at most 6 significant bits), or stay constant"}
     out["layer_16384_tokens"] = layer_at(nv, W, 2 * M, signs, max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)

@@ -73,16 +73,64 @@ __global__ __launch_bounds__(kPeakThreads, 1) void mfma_f16_loop_kernel(int iter
   if (s == 1234.5f) sink[blockIdx.x] = s;  // keeps the loop; never true in practice
 }
 
+// The same MFMAs with no VALU work in the loop: the operands alternate
+// between two register sets of random-looking values (bits under `mask`
+// random, the rest as above), so every MFMA sees other bits than the one
+// before at no instruction cost; mask 0 makes both sets equal (constant
+// operands).  This is the fp16 MFMA rate the card holds when nothing else
+// competes for issue or power.
+__global__ __launch_bounds__(kPeakThreads, 1) void mfma_f16_pure_kernel(int iters, uint32_t mask,
+                                                                      float* sink) {
+  float16_t acc[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  uint32_t x = (blockIdx.x * kPeakThreads + threadIdx.x) * 0x9E3779B9u + 0x7F4A7C15u;
+  half8_t o[2][8];
+#pragma unroll
+  for (int set = 0; set < 2; ++set)
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      u32x4_t v;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        x ^= x << 13;
+        x ^= x >> 17;
+        x ^= x << 5;
+        v[d] = ((set == 0 ? x : x ^ 0xFFFFFFFFu) & mask) | 0x30003000u;
+      }
+      __builtin_memcpy(&o[set][f], &v, 16);
+    }
+  for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+    for (int set = 0; set < 2; ++set)
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o[set][c >> 2], o[set][4 + (c & 3)], acc[c],
+                                                        0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) s += acc[c][0];
+  if (s == 1234.5f) sink[blockIdx.x] = s;  // keeps the loop; never true in practice
+}
+
 }  // namespace
 
 extern "C" {
 
-nvfp4_status nvfp4_peak_mfma_f16(int32_t iters, uint32_t toggle_mask, float* sink, double* flops,
-                                 void* stream) {
+nvfp4_status nvfp4_peak_mfma_f16(int32_t iters, uint32_t toggle_mask, int32_t valu_per_mfma,
+                                 float* sink, double* flops, void* stream) {
   if (!sink || !flops) return NVFP4_ERR_NULL;
   if (iters <= 0) return NVFP4_ERR_SHAPE;
-  hipLaunchKernelGGL(mfma_f16_loop_kernel, dim3(kBlocks), dim3(kPeakThreads), 0,
-                     static_cast<hipStream_t>(stream), iters, toggle_mask & 0x87FF87FFu, sink);
+  if (valu_per_mfma != 0 && valu_per_mfma != 4) return NVFP4_ERR_DTYPE;
+  if (valu_per_mfma == 4)
+    hipLaunchKernelGGL(mfma_f16_loop_kernel, dim3(kBlocks), dim3(kPeakThreads), 0,
+                       static_cast<hipStream_t>(stream), iters, toggle_mask & 0x87FF87FFu, sink);
+  else
+    hipLaunchKernelGGL(mfma_f16_pure_kernel, dim3(kBlocks), dim3(kPeakThreads), 0,
+                       static_cast<hipStream_t>(stream), iters, toggle_mask & 0x87FF87FFu, sink);
   if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
   *flops = (double)kBlocks * (kPeakThreads / 64) * ((iters + 1) / 2 * 2) * 16 * (2.0 * 32 * 32 * 16);
   return NVFP4_OK;

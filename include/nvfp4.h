@@ -396,18 +396,23 @@ nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* c
 /*
  * nvfp4_peak_mfma_f16: measurement helper, not part of the layer.  Enqueues
  * an fp16 MFMA loop shaped like the GEMM's inner loop
- * (v_mfma_f32_32x32x16_f16, FP32 accumulation, one wave per SIMD, no memory
- * traffic, random-looking operands that change every iteration) of `iters`
- * iterations and returns in *flops the floating-point operations it
- * performs; timing it on the stream gives the compute ceiling the card holds
- * under sustained MFMA load, next to the datasheet peak.  toggle_mask picks
- * the operand bits that change (ANDed with 0x87FF87FF, the sign and mantissa
- * bits of two f16): 0 runs the same instructions on constant operands.
- * sink: a device buffer of 2048 floats the kernel may write (it does not in
- * practice).
+ * (v_mfma_f32_32x32x16_f16, FP32 accumulation, one wave per SIMD, 16
+ * accumulators, no memory traffic) of `iters` iterations and returns in
+ * *flops the floating-point operations it performs; timing it on the stream
+ * gives the compute rate the card holds under that load, next to the
+ * datasheet peak (which assumes the top clock).  toggle_mask picks the
+ * operand bits that change (ANDed with 0x87FF87FF, the sign and mantissa bits
+ * of two f16; 0 keeps the operands constant).  valu_per_mfma:
+ *   0  no VALU work in the loop: the operands alternate between two random
+ *      register sets, so each MFMA sees new bits at no instruction cost
+ *      (the pure MFMA rate);
+ *   4  four VALU instructions per MFMA make fresh random operands every
+ *      iteration (about the GEMM's dequantisation load).
+ * Any other value is NVFP4_ERR_DTYPE.  sink: a device buffer of 2048 floats
+ * the kernel may write (it does not in practice).
  */
-nvfp4_status nvfp4_peak_mfma_f16(int32_t iters, uint32_t toggle_mask, float* sink, double* flops,
-                                 void* stream);
+nvfp4_status nvfp4_peak_mfma_f16(int32_t iters, uint32_t toggle_mask, int32_t valu_per_mfma,
+                                 float* sink, double* flops, void* stream);
 
 #ifdef __cplusplus
 }

@@ -240,9 +240,10 @@ def test_linear_ctx_bytes_and_init():
 def test_peak_helper_argument_errors():
     flops = ctypes.c_double(0)
     f = nv._lib.nvfp4_peak_mfma_f16
-    assert f(100, 0, None, ctypes.byref(flops), None) == nv.ERR_NULL
-    assert f(100, 0, P, None, None) == nv.ERR_NULL
-    assert f(0, 0, P, ctypes.byref(flops), None) == nv.ERR_SHAPE
+    assert f(100, 0, 4, None, ctypes.byref(flops), None) == nv.ERR_NULL
+    assert f(100, 0, 4, P, None, None) == nv.ERR_NULL
+    assert f(0, 0, 4, P, ctypes.byref(flops), None) == nv.ERR_SHAPE
+    assert f(100, 0, 2, P, ctypes.byref(flops), None) == nv.ERR_DTYPE
 
 
 def test_quantize_static_argument_errors():

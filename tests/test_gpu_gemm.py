@@ -187,3 +187,5 @@ def test_mfma_loop_ceiling(nv):
     nv.nvfp4_peak_mfma_f16(200)
     tf = nv.nvfp4_peak_mfma_f16(2000)
     assert 500.0 < tf < 2600.0, tf
+    pure = nv.nvfp4_peak_mfma_f16(2000, valu_per_mfma=0)
+    assert 500.0 < pure < 2600.0, pure
