@@ -453,6 +453,10 @@ def main():
     mfma_loop = nv.nvfp4_peak_mfma_f16(5000)
     mfma_6bit = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0x87E087E0)
     mfma_const = nv.nvfp4_peak_mfma_f16(5000, toggle_mask=0, valu_per_mfma=0)
+    nv.nvfp4_peak_mfma_fp4(500)
+    mfma_fp4 = nv.nvfp4_peak_mfma_fp4(2500)
+    mx = out["mxfp4_comparator"]
+    mx["frac_of_fp4_loop"] = round(mx["gemm_TFLOPs"] / mfma_fp4, 4)
     out["measured_ceiling"] = {
         "hbm_copy_GBps": round(copy_gbps, 1),
         "mfma_f16_pure_TFLOPs": round(mfma_pure, 1),
@@ -462,13 +466,16 @@ def main():
         "mfma_f16_4valu_6bit_operands_TFLOPs": round(mfma_6bit, 1),
         "gemm_frac_of_pure": round(achieved / mfma_pure, 4),
         "gemm_frac_of_pure_6bit": round(achieved / mfma_pure_6bit, 4),
+        "mfma_fp4_scaled_pure_TFLOPs": round(mfma_fp4, 1),
         "note": "hbm_copy: torch's device copy of 1 GiB (reads and writes 1 GiB), median of 5, "
                 "HIP events. mfma: an fp16 32x32x16 MFMA loop with 16 accumulators per wave and "
                 "one wave per SIMD, as the GEMM runs; 'pure' issues no VALU between MFMAs, "
                 "'4valu' issues 4 independent VALU ops after each; operands alternate between "
                 "two register sets differing in sign, one exponent bit and all mantissa bits, or "
                 "in sign, that exponent bit and the top 5 mantissa bits (the bit pattern of "
-                "dequantised E2M1 x E4M3 values, at most 6 significant bits), or stay constant"}
+                "dequantised E2M1 x E4M3 values, at most 6 significant bits), or stay constant. "
+                "mfma_fp4_scaled: the MXFP4 comparator's scaled FP4 MFMA (32x32x64, E2M1 x E2M1, "
+                "unit scales) in the same VALU-free loop, all code bits toggling"}
     out["layer_16384_tokens"] = layer_at(nv, W, 2 * M, signs, max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)

@@ -139,6 +139,47 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, uint32_t dpair, boo
   return o;
 }
 
+// Pairs p0 and p0+1 (p0 = 0 or 2) of word w, times the fp16 scale in half
+// `HI` of dpair: both converts first, then both multiplies, so that no
+// multiply waits on the convert just before it (back-to-back dependent
+// pairs measured ~5% slower in an MFMA-interleaved loop).  Written as one asm
+// block because the compiler's scheduler otherwise interleaves each convert
+// with its multiply through one temporary register.  The values are those of
+// dequant_pair.  o0 is written before dpair's last read, hence early-clobber.
+template <int P0, bool HI>
+__device__ __forceinline__ void dequant_2pairs(uint32_t w, uint32_t dpair, uint32_t& o0,
+                                               uint32_t& o1) {
+  uint32_t t0, t1;
+  if (P0 == 0 && !HI)
+    asm volatile(
+        "v_cvt_scalef32_pk_f16_fp4 %2, %4, 1.0\n\t"
+        "v_cvt_scalef32_pk_f16_fp4 %3, %4, 1.0 op_sel:[1,0,0]\n\t"
+        "v_pk_mul_f16 %0, %5, %2 op_sel_hi:[0,1]\n\t"
+        "v_pk_mul_f16 %1, %5, %3 op_sel_hi:[0,1]"
+        : "=&v"(o0), "=v"(o1), "=&v"(t0), "=&v"(t1) : "v"(w), "v"(dpair));
+  else if (P0 == 2 && !HI)
+    asm volatile(
+        "v_cvt_scalef32_pk_f16_fp4 %2, %4, 1.0 op_sel:[0,1,0]\n\t"
+        "v_cvt_scalef32_pk_f16_fp4 %3, %4, 1.0 op_sel:[1,1,0]\n\t"
+        "v_pk_mul_f16 %0, %5, %2 op_sel_hi:[0,1]\n\t"
+        "v_pk_mul_f16 %1, %5, %3 op_sel_hi:[0,1]"
+        : "=&v"(o0), "=v"(o1), "=&v"(t0), "=&v"(t1) : "v"(w), "v"(dpair));
+  else if (P0 == 0)
+    asm volatile(
+        "v_cvt_scalef32_pk_f16_fp4 %2, %4, 1.0\n\t"
+        "v_cvt_scalef32_pk_f16_fp4 %3, %4, 1.0 op_sel:[1,0,0]\n\t"
+        "v_pk_mul_f16 %0, %5, %2 op_sel:[1,0] op_sel_hi:[1,1]\n\t"
+        "v_pk_mul_f16 %1, %5, %3 op_sel:[1,0] op_sel_hi:[1,1]"
+        : "=&v"(o0), "=v"(o1), "=&v"(t0), "=&v"(t1) : "v"(w), "v"(dpair));
+  else
+    asm volatile(
+        "v_cvt_scalef32_pk_f16_fp4 %2, %4, 1.0 op_sel:[0,1,0]\n\t"
+        "v_cvt_scalef32_pk_f16_fp4 %3, %4, 1.0 op_sel:[1,1,0]\n\t"
+        "v_pk_mul_f16 %0, %5, %2 op_sel:[1,0] op_sel_hi:[1,1]\n\t"
+        "v_pk_mul_f16 %1, %5, %3 op_sel:[1,0] op_sel_hi:[1,1]"
+        : "=&v"(o0), "=v"(o1), "=&v"(t0), "=&v"(t1) : "v"(w), "v"(dpair));
+}
+
 // MFMA sub-step S of a K-step, written in issue order: chunk G (0 .. 4 NB-1)
 // issues MFMA (G / NB, G % NB) on `src`, then dequantises the next
 // sub-step's fragment pairs PP G .. PP G + PP-1 into `dst` (PP = 2 for NB = 4,
@@ -164,14 +205,24 @@ __device__ __forceinline__ void sub_step(float16_t (&acc)[4][NB], const FragsT<N
                                                             as_half8(src.w[4 + j]), acc[i][j], 0, 0, 0);
     if (S == 0) mem(G);
     if (S == 1) mem2(G);
+    if (PP == 2) {
+      // the chunk's two pairs are pairs 2 (G % 2), +1 of block G / 2
+      const int b = G >> 1;
+      constexpr bool kHi = S + 1 >= 2 && S < 3;
+      if (S == 3 && (G & 1) == 0) dp[b] = nxt_in_k ? scale_pair(scale_of(nxt, b), sel) : 0u;
+      const uint32_t w = S < 3 ? word_of(cur, b, S + 1) : word_of(nxt, b, 0);
+      if (G & 1) dequant_2pairs<2, kHi>(w, dp[b], dst.w[b][2], dst.w[b][3]);
+      else dequant_2pairs<0, kHi>(w, dp[b], dst.w[b][0], dst.w[b][1]);
+    } else {
 #pragma unroll
-    for (int q = 0; q < PP; ++q) {
-      const int P = PP * G + q, b = P >> 2, p = P & 3;
-      if (S < 3) {
-        dst.w[b][p] = dequant_pair(word_of(cur, b, S + 1), dp[b], S + 1 >= 2, p);
-      } else {
-        if (p == 0) dp[b] = nxt_in_k ? scale_pair(scale_of(nxt, b), sel) : 0u;
-        dst.w[b][p] = dequant_pair(word_of(nxt, b, 0), dp[b], false, p);
+      for (int q = 0; q < PP; ++q) {
+        const int P = PP * G + q, b = P >> 2, p = P & 3;
+        if (S < 3) {
+          dst.w[b][p] = dequant_pair(word_of(cur, b, S + 1), dp[b], S + 1 >= 2, p);
+        } else {
+          if (p == 0) dp[b] = nxt_in_k ? scale_pair(scale_of(nxt, b), sel) : 0u;
+          dst.w[b][p] = dequant_pair(word_of(nxt, b, 0), dp[b], false, p);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);

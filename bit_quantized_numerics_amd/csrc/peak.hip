@@ -116,9 +116,60 @@ __global__ __launch_bounds__(kPeakThreads, 1) void mfma_f16_pure_kernel(int iter
   if (s == 1234.5f) sink[blockIdx.x] = s;  // keeps the loop; never true in practice
 }
 
+// The MXFP4 comparator's instruction, v_mfma_scale_f32_32x32x64_f8f6f4 with
+// both operands E2M1 (format 4) and unit E8M0 scales (127), in the same
+// VALU-free form: 16 accumulators, operands alternating between two register
+// sets that differ in the bits under `mask`.
+__global__ __launch_bounds__(kPeakThreads, 1) void mfma_fp4_pure_kernel(int iters, uint32_t mask,
+                                                                      float* sink) {
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  float16_t acc[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  uint32_t x = (blockIdx.x * kPeakThreads + threadIdx.x) * 0x9E3779B9u + 0x2545F491u;
+  v8i o[2][8];
+#pragma unroll
+  for (int set = 0; set < 2; ++set)
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        x ^= x << 13;
+        x ^= x >> 17;
+        x ^= x << 5;
+        o[set][f][d] = d < 4 ? (int)((set == 0 ? x : x ^ 0xFFFFFFFFu) & mask) : 0;
+      }
+    }
+  for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+    for (int set = 0; set < 2; ++set)
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o[set][c >> 2], o[set][4 + (c & 3)],
+                                                                 acc[c], 4, 4, 0, 127, 0, 127);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) s += acc[c][0];
+  if (s == 1234.5f) sink[blockIdx.x] = s;  // keeps the loop; never true in practice
+}
+
 }  // namespace
 
 extern "C" {
+
+nvfp4_status nvfp4_peak_mfma_fp4(int32_t iters, uint32_t toggle_mask, float* sink, double* flops,
+                                 void* stream) {
+  if (!sink || !flops) return NVFP4_ERR_NULL;
+  if (iters <= 0) return NVFP4_ERR_SHAPE;
+  hipLaunchKernelGGL(mfma_fp4_pure_kernel, dim3(kBlocks), dim3(kPeakThreads), 0,
+                     static_cast<hipStream_t>(stream), iters, toggle_mask, sink);
+  if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
+  *flops = (double)kBlocks * (kPeakThreads / 64) * ((iters + 1) / 2 * 2) * 16 * (2.0 * 32 * 32 * 64);
+  return NVFP4_OK;
+}
 
 nvfp4_status nvfp4_peak_mfma_f16(int32_t iters, uint32_t toggle_mask, int32_t valu_per_mfma,
                                  float* sink, double* flops, void* stream) {

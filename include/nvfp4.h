@@ -346,6 +346,8 @@ nvfp4_status nvfp4_rht16(const void* x, float* y, int32_t in_dtype, int64_t rows
  * gfx950's scaled FP4 MFMA; that path needs K % 128 == 0, K >= 384 and
  * rows * K / 2 < 2^31 for each operand (else NVFP4_ERR_SHAPE), and mixing an
  * MX32 operand with an NVFP4 one is NVFP4_ERR_DTYPE.
+ * workspace, ws_bytes: reserved, not read or written (no GEMM path uses
+ * scratch memory); NULL and 0 are accepted.
  */
 nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int32_t c_dtype,
                         int64_t ldc, void* workspace, size_t ws_bytes, void* stream);
@@ -413,6 +415,20 @@ nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* c
  */
 nvfp4_status nvfp4_peak_mfma_f16(int32_t iters, uint32_t toggle_mask, int32_t valu_per_mfma,
                                  float* sink, double* flops, void* stream);
+
+/*
+ * nvfp4_peak_mfma_fp4: measurement helper, not part of the layer.  The same
+ * VALU-free loop on the MXFP4 comparator's instruction,
+ * v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 x E2M1 operands and unit E8M0
+ * scales (one wave per SIMD, 16 accumulators, `iters` iterations, no memory
+ * traffic); operands alternate between two register sets differing in the
+ * bits under toggle_mask (0 keeps them constant; every 4-bit pattern is a
+ * finite E2M1 code).  *flops receives 2*32*32*64 per MFMA.  sink: a device
+ * buffer of 2048 floats the kernel may write (it does not in practice).
+ * NVFP4_ERR_NULL / NVFP4_ERR_SHAPE (iters <= 0) as for nvfp4_peak_mfma_f16.
+ */
+nvfp4_status nvfp4_peak_mfma_fp4(int32_t iters, uint32_t toggle_mask, float* sink, double* flops,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

@@ -244,6 +244,10 @@ def test_peak_helper_argument_errors():
     assert f(100, 0, 4, P, None, None) == nv.ERR_NULL
     assert f(0, 0, 4, P, ctypes.byref(flops), None) == nv.ERR_SHAPE
     assert f(100, 0, 2, P, ctypes.byref(flops), None) == nv.ERR_DTYPE
+    g = nv._lib.nvfp4_peak_mfma_fp4
+    assert g(100, 0, None, ctypes.byref(flops), None) == nv.ERR_NULL
+    assert g(100, 0, P, None, None) == nv.ERR_NULL
+    assert g(-1, 0, P, ctypes.byref(flops), None) == nv.ERR_SHAPE
 
 
 def test_quantize_static_argument_errors():

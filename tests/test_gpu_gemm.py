@@ -189,3 +189,5 @@ def test_mfma_loop_ceiling(nv):
     assert 500.0 < tf < 2600.0, tf
     pure = nv.nvfp4_peak_mfma_f16(2000, valu_per_mfma=0)
     assert 500.0 < pure < 2600.0, pure
+    fp4 = nv.nvfp4_peak_mfma_fp4(500)
+    assert 1000.0 < fp4 < 10200.0, fp4
