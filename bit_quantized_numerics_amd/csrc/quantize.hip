@@ -370,11 +370,74 @@ __device__ __forceinline__ bool emit_tile(int64_t rows, int64_t cols, int64_t* t
 
 typedef __amdgpu_buffer_rsrc_t out_rsrc_t;
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Raw buffer over an output region starting at `base` (stores take a per-lane
 // offset and a scalar one; validity is decided by the caller's lane mask).
 __device__ __forceinline__ out_rsrc_t out_rsrc(void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, -1, 0x00020000);
+}
+
+// ---- LDS staging of the column (transposed) copy.  A workgroup's column
+// copy is 256 output rows (its source columns) of TR/2 code bytes (its
+// tokens) and, for 1x16 blocks, TR/16 scale bytes.  Every thread computes
+// 8 output rows' 16-token blocks (8 code bytes and one scale byte each); they
+// are gathered in LDS and stored as contiguous row segments (64 or 128 bytes
+// of codes, 8 bytes of scales) instead of one 8-byte store per block.
+//
+// Codes: output row R at dword col_code_base(R) (two dwords of padding per 8
+// rows), its 8-byte chunk c at position c ^ x(R), x(R) = bit 2 (64-byte rows)
+// or bit 1 (128-byte rows) of R.  A thread's 8-byte write (rows R = 8 cg + j,
+// one per lane, so x is the same in every lane) lands in 32 distinct bank
+// pairs; when half a wave reads the first 8 bytes of its 16-byte units (8 or
+// 4 rows), the rows whose windows coincide modulo the 64 banks differ in x and
+// so read the other half of each unit: every bank at most once.
+template <int TR>
+__device__ __forceinline__ int col_code_base(int R) {
+  return (TR / 8) * R + 2 * (R >> 3);
+}
+template <int TR>
+__device__ __forceinline__ int col_code_dw(int R, int chunk8) {  // chunk8: 8-byte unit in the row
+  const int x = TR == 128 ? ((R >> 2) & 1) : ((R >> 1) & 1);
+  return col_code_base<TR>(R) + 2 * (chunk8 ^ x);
+}
+template <int TR>
+constexpr int col_code_words() {
+  return (TR / 8) * 256 + 2 * 32;
+}
+// Scales (1x16 blocks): row R's TR/16 bytes at (TR/16) R + 4 (R >> 3), so
+// the byte writes of one instruction hit 32 distinct dwords ((TR/64 + 1) cg
+// + const, an odd multiplier).
+template <int TR>
+__device__ __forceinline__ int col_scale_byte(int R) { return (TR / 16) * R + 4 * (R >> 3); }
+template <int TR>
+constexpr int col_scale_bytes() { return (TR / 16) * 256 + 4 * 32; }
+
+// Stores the staged codes of the workgroup's column copy: `nrows` output
+// rows (<= 256) of `seg` bytes (TR/2, or fewer for a ragged last tile, a
+// multiple of 8), each row `pitch` bytes apart in the copy from `base`.
+template <int TR>
+__device__ __forceinline__ void store_col_codes(const uint32_t* cst, uint8_t* base, int64_t pitch,
+                                                int nrows, int seg) {
+  constexpr int kUnits = TR / 32;                 // 16-byte units per row: 4 or 8
+  constexpr int kRowsPerPass = 2 * TR / kUnits;   // threads / units
+  const int t = threadIdx.x, q = t % kUnits;
+  const out_rsrc_t o = out_rsrc(base);
+#pragma unroll
+  for (int k = 0; k < 256 / kRowsPerPass; ++k) {
+    const int R = t / kUnits + kRowsPerPass * k;
+    if (R < nrows && 16 * q < seg) {
+      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(&cst[col_code_dw<TR>(R, 2 * q)]);
+      const uint32_t vo = (uint32_t)(R * pitch) + 16u * (uint32_t)q;
+      if (16 * q + 16 <= seg) {
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(&cst[col_code_dw<TR>(R, 2 * q + 1)]);
+        const u32x4_t v = {lo[0], lo[1], hi[0], hi[1]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, o, vo, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b64(lo, o, vo, 0, 0);
+      }
+    }
+  }
 }
 
 // Element multipliers r = s_enc / d for every E4M3 code d (0 for d = 0,
@@ -397,6 +460,9 @@ void quant_tile_kernel(TileArgs a) {
   constexpr bool ROW = F & kFRow, COL = F & kFCol, TWO_D = F & kF2D, RHT = F & kFRht;
   constexpr bool SR_ROW = F & kFSrRow, SR_COL = F & kFSrCol, RHT4 = F & kFRht4;
   __shared__ float rtab[2][128];
+  // column-copy staging (used by the flag sets with a column copy)
+  __shared__ __align__(16) uint32_t cst[COL ? col_code_words<TR>() : 1];
+  __shared__ __align__(16) uint8_t csc[(COL && !TWO_D) ? col_scale_bytes<TR>() : 1];
 
   const int t = threadIdx.x, cg = t & 31, rs = t >> 5;
   const int64_t rows = a.rows, cols = a.cols;
@@ -456,83 +522,54 @@ void quant_tile_kernel(TileArgs a) {
     // keep the unpacking below this point: hoisted above the table read it
     // would hold all 128 values at once (occupancy halves)
     __builtin_amdgcn_sched_barrier(0);
+    // The column (transposed) copy first: staged in LDS, its stores are in
+    // flight while the row copy is computed.  Both copies are the same
+    // products read in two directions; the second recomputes them from the
+    // packed patch rather than keeping them (128 more registers): the empty
+    // asm hides that its r and zero sign mask (unpacking through the signed
+    // form) repeat the first one's values.
+    if (COL) {
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float s16[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s16[i] = patch_elem(p, i, j) * r;
+          const u32x2_t w = {fp4x8_rn(s16), fp4x8_rn(s16 + 8)};
+          *reinterpret_cast<u32x2_t*>(&cst[col_code_dw<TR>(8 * cg + j, rs)]) = w;
+        }
+      }
+      __syncthreads();
+      store_col_codes<TR>(cst, a.col.codes + tile_c0 * (rows / 2) + tile_r0 / 2, rows / 2,
+                          (int)min(cols - tile_c0, (int64_t)256),
+                          (int)min(rows - tile_r0, (int64_t)TR) / 2);
+    }
     if (valid) {
       const int64_t gcols = cols / 16, grows = rows / 16;
+      if ((cg & 1) == 0) {
+        if (ROW) a.row.scales[(r0 / 16) * gcols + c0 / 16] = (uint8_t)dcode;
+        if (COL) a.col.scales[(c0 / 16) * grows + r0 / 16] = (uint8_t)dcode;
+      }
       if (ROW) {
+        float rr = r;
+        uint32_t z = 0;
+        asm volatile("" : "+v"(rr), "+v"(z));
         const out_rsrc_t oc = out_rsrc(a.row.codes + tile_r0 * (cols / 2) + tile_c0 / 2);
         const uint32_t vo = (uint32_t)(rs * 16 * (cols / 2) + cg * 4);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float s8[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) s8[j] = patch_elem(p, i, j) * r;
+          for (int j = 0; j < 8; ++j) s8[j] = patch_elem_s(p, i, j, z) * rr;
           __builtin_amdgcn_raw_buffer_store_b32(fp4x8_rn(s8), oc, vo, (uint32_t)(i * (cols / 2)), 0);
-        }
-      }
-      if ((cg & 1) == 0) {
-        if (ROW) a.row.scales[(r0 / 16) * gcols + c0 / 16] = (uint8_t)dcode;
-        if (COL) a.col.scales[(c0 / 16) * grows + r0 / 16] = (uint8_t)dcode;
-      }
-      if (COL) {
-        // The same products as the row copy, read down each column.  They are
-        // recomputed from the packed patch rather than kept (128 more
-        // registers): the empty asm hides that r and the zero sign mask
-        // (unpacking through the signed form) repeat the row copy's values.
-        float rc = r;
-        uint32_t z = 0;
-        asm volatile("" : "+v"(rc), "+v"(z));
-        const out_rsrc_t oc = out_rsrc(a.col.codes + tile_c0 * (rows / 2) + tile_r0 / 2);
-        const uint32_t vo = (uint32_t)(cg * 8 * (rows / 2) + rs * 8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float s16[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s16[i] = patch_elem_s(p, i, j, z) * rc;
-          const u32x2_t w = {fp4x8_rn(s16), fp4x8_rn(s16 + 8)};
-          __builtin_amdgcn_raw_buffer_store_b64(w, oc, vo, (uint32_t)(j * (rows / 2)), 0);
         }
       }
     }
   } else {
-    // ---- row-wise copy: 1x16 blocks along cols [Review s1 Steps 2-3]
-    if (ROW && do_row) {
-      const out_rsrc_t oc = out_rsrc(a.row.codes + tile_r0 * (cols / 2) + tile_c0 / 2);
-      const out_rsrc_t os = out_rsrc(a.row.scales + tile_r0 * (cols / 16) + tile_c0 / 16);
-      const uint32_t vo = (uint32_t)(rs * 16 * (cols / 2) + cg * 4);
-      const uint32_t vs = (uint32_t)(rs * 16 * (cols / 16) + (cg >> 1));
-      const uint64_t e0 = a.row.offset + (uint64_t)(r0 * cols + c0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x[8];
-        float am = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          x[j] = patch_elem(p, i, j);
-          am = fmaxf(am, __builtin_fabsf(x[j]));
-        }
-        am = fmaxf(am, lane_xor1(am));
-        const uint32_t dcode = e4m3_code(am * tr.s6);
-        const float r = rtab[0][dcode];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = x[j] * r;
-        uint32_t w;
-        if (SR_ROW)
-          w = fp4x8_sr2(x, sr_draw8_n02(a.row.seed, a.row.stream, e0 + (uint64_t)(i * cols)));
-        else
-          w = fp4x8_rn(x);
-        if (valid && r0 + i < rows) {
-          __builtin_amdgcn_raw_buffer_store_b32(w, oc, vo, (uint32_t)(i * (cols / 2)), 0);
-          if ((cg & 1) == 0)
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)dcode, os, vs, (uint32_t)(i * (cols / 16)), 0);
-        }
-      }
-    }
-    // ---- column-wise copy: 1x16 blocks along rows, optional RHT [Review s3]
+    // ---- column-wise copy: 1x16 blocks along rows, optional RHT [Review s3].
+    // First, so that its stores (issued after the workgroup barrier) are in
+    // flight while the row copy is computed.
     if (COL && do_col) {
-      const out_rsrc_t oc = out_rsrc(a.col.codes + tile_c0 * (rows / 2) + tile_r0 / 2);
-      const out_rsrc_t os = out_rsrc(a.col.scales + tile_c0 * (rows / 16) + tile_r0 / 16);
-      const uint32_t vo = (uint32_t)(cg * 8 * (rows / 2) + rs * 8);
-      const uint32_t vs = (uint32_t)(cg * 8 * (rows / 16) + rs);
       const uint64_t e0 = a.col.offset + (uint64_t)(c0 * rows + r0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -568,12 +605,78 @@ void quant_tile_kernel(TileArgs a) {
           w[0] = fp4x8_rn(u);
           w[1] = fp4x8_rn(u + 8);
         }
-        if (valid) {
-          __builtin_amdgcn_raw_buffer_store_b64(w, oc, vo, (uint32_t)(j * (rows / 2)), 0);
-          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)dcode, os, vs, (uint32_t)(j * (rows / 16)), 0);
+        // every lane stages its blocks; those of lanes past the operand fall
+        // outside the stored window
+        const int R = 8 * cg + j;
+        *reinterpret_cast<u32x2_t*>(&cst[col_code_dw<TR>(R, rs)]) = w;
+        csc[col_scale_byte<TR>(R) + rs] = (uint8_t)dcode;
+      }
+      __syncthreads();
+      const int nrows = (int)min(cols - tile_c0, (int64_t)256);
+      const int ntok = (int)min(rows - tile_r0, (int64_t)TR);
+      store_col_codes<TR>(cst, a.col.codes + tile_c0 * (rows / 2) + tile_r0 / 2, rows / 2, nrows,
+                          ntok / 2);
+      // scales: thread t stores output row t's TR/16 bytes
+      if (t < nrows) {
+        constexpr int kW = TR / 64;  // scale dwords per row: 2 or 4
+        const int nb = ntok / 16;
+        uint32_t sw[kW];
+#pragma unroll
+        for (int q = 0; q < kW; ++q)
+          sw[q] = *reinterpret_cast<const uint32_t*>(&csc[col_scale_byte<TR>(t) + 4 * q]);
+        uint8_t* rowp = a.col.scales + (tile_c0 + t) * (rows / 16) + tile_r0 / 16;
+        const out_rsrc_t os = out_rsrc(rowp);
+        if (nb == TR / 16 && ((uintptr_t)rowp & (4 * kW - 1)) == 0) {
+          if (kW == 2) {
+            const u32x2_t v = {sw[0], sw[1]};
+            __builtin_amdgcn_raw_buffer_store_b64(v, os, 0, 0, 0);
+          } else {
+            const u32x4_t v = {sw[0], sw[1], sw[kW > 2 ? 2 : 0], sw[kW > 3 ? 3 : 0]};
+            __builtin_amdgcn_raw_buffer_store_b128(v, os, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < TR / 16; ++b)
+            if (b < nb)
+              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(sw[b >> 2] >> (8 * (b & 3))), os,
+                                                   (uint32_t)b, 0, 0);
         }
       }
     }
+    // ---- row-wise copy: 1x16 blocks along cols [Review s1 Steps 2-3]
+    if (ROW && do_row) {
+      const out_rsrc_t oc = out_rsrc(a.row.codes + tile_r0 * (cols / 2) + tile_c0 / 2);
+      const out_rsrc_t os = out_rsrc(a.row.scales + tile_r0 * (cols / 16) + tile_c0 / 16);
+      const uint32_t vo = (uint32_t)(rs * 16 * (cols / 2) + cg * 4);
+      const uint32_t vs = (uint32_t)(rs * 16 * (cols / 16) + (cg >> 1));
+      const uint64_t e0 = a.row.offset + (uint64_t)(r0 * cols + c0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x[8];
+        float am = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x[j] = patch_elem(p, i, j);
+          am = fmaxf(am, __builtin_fabsf(x[j]));
+        }
+        am = fmaxf(am, lane_xor1(am));
+        const uint32_t dcode = e4m3_code(am * tr.s6);
+        const float r = rtab[0][dcode];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = x[j] * r;
+        uint32_t w;
+        if (SR_ROW)
+          w = fp4x8_sr2(x, sr_draw8_n02(a.row.seed, a.row.stream, e0 + (uint64_t)(i * cols)));
+        else
+          w = fp4x8_rn(x);
+        if (valid && r0 + i < rows) {
+          __builtin_amdgcn_raw_buffer_store_b32(w, oc, vo, (uint32_t)(i * (cols / 2)), 0);
+          if ((cg & 1) == 0)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)dcode, os, vs, (uint32_t)(i * (cols / 16)), 0);
+        }
+      }
+    }
+
   }
 }
 
