@@ -624,22 +624,26 @@ void quant_tile_kernel(TileArgs a) {
 #pragma unroll
         for (int q = 0; q < kW; ++q)
           sw[q] = *reinterpret_cast<const uint32_t*>(&csc[col_scale_byte<TR>(t) + 4 * q]);
-        uint8_t* rowp = a.col.scales + (tile_c0 + t) * (rows / 16) + tile_r0 / 16;
-        const out_rsrc_t os = out_rsrc(rowp);
-        if (nb == TR / 16 && ((uintptr_t)rowp & (4 * kW - 1)) == 0) {
+        // a workgroup-uniform base with per-lane offsets (a per-lane
+        // descriptor would make the compiler loop over the lanes)
+        uint8_t* sbase = a.col.scales + tile_c0 * (rows / 16) + tile_r0 / 16;
+        const out_rsrc_t os = out_rsrc(sbase);
+        const uint32_t vo = (uint32_t)(t * (rows / 16));
+        const bool aligned = ((uintptr_t)sbase % (4 * kW)) == 0 && (rows / 16) % (4 * kW) == 0;
+        if (nb == TR / 16 && aligned) {
           if (kW == 2) {
             const u32x2_t v = {sw[0], sw[1]};
-            __builtin_amdgcn_raw_buffer_store_b64(v, os, 0, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(v, os, vo, 0, 0);
           } else {
             const u32x4_t v = {sw[0], sw[1], sw[kW > 2 ? 2 : 0], sw[kW > 3 ? 3 : 0]};
-            __builtin_amdgcn_raw_buffer_store_b128(v, os, 0, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, os, vo, 0, 0);
           }
         } else {
 #pragma unroll
           for (int b = 0; b < TR / 16; ++b)
             if (b < nb)
               __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(sw[b >> 2] >> (8 * (b & 3))), os,
-                                                   (uint32_t)b, 0, 0);
+                                                   vo + (uint32_t)b, 0, 0);
         }
       }
     }
