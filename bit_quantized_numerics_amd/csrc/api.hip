@@ -648,8 +648,14 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
   if (fx) {
     NVFP4_HIP(launch_amax(x, dtype, M, K, K, recipe->rht_signs, ws_word(workspace, kSlotXRaw),
                           x_rht ? ws_word(workspace, kSlotXRht) : nullptr, s));
-    NVFP4_HIP(launch_quant_tile(dtype, fx, ax, s));
   }
+  // W's stats pass runs before X's emit pass: it then reads right after
+  // another read (X's stats) instead of after the emit's writes, whose dirty
+  // lines it would otherwise write back while it reads (measured ~20 us
+  // faster per forward).
+  const bool w_any = !bf16_fprop || want_wt;
+  if (w_any) NVFP4_HIP(launch_amax(w, dtype, N, K, K, 0, ws_word(workspace, kSlotW), nullptr, s));
+  if (fx) NVFP4_HIP(launch_quant_tile(dtype, fx, ax, s));
 
   // W: 16x16 scales, with the transposed copy for Dgrad when training.  The
   // BF16 forward keeps only W^T (1x16 along N on its own with no_2d_weights).
@@ -664,7 +670,6 @@ nvfp4_status nvfp4_linear_fwd(const void* x, const void* w, void* y, int64_t M, 
     aw.status = ws_word(workspace, kSlotStatus);
     if (!bf16_fprop) aw.row = copy_args(&ctx->wq, workspace, kSlotW, nullptr);
     if (want_wt) aw.col = copy_args(&ctx->wqt, workspace, kSlotW, nullptr);
-    NVFP4_HIP(launch_amax(w, dtype, N, K, K, 0, ws_word(workspace, kSlotW), nullptr, s));
     NVFP4_HIP(launch_quant_tile(dtype, fw, aw, s));
   }
 
