@@ -56,7 +56,11 @@ class c_linear_ctx(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("xq", c_tensor), ("wq", c_tensor), ("wqt", c_tensor), ("xqt", c_tensor),
                 ("dyq", c_tensor), ("dyqt", c_tensor), ("rht_signs", ctypes.c_uint32),
-                ("rht", ctypes.c_int32)]
+                ("rht", ctypes.c_int32), ("wgrad_scratch", ctypes.c_void_p),
+                ("wgrad_scratch_bytes", ctypes.c_size_t)]
+
+
+LINEAR_SCRATCH_BYTES = 32 << 20  # NVFP4_LINEAR_SCRATCH_BYTES
 
 
 _vp, _i64, _i32, _u32, _u64, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
@@ -410,8 +414,10 @@ class LinearContext:
         self.xqt = NVFP4Tensor(K, M, device=device)
         self.dyq = NVFP4Tensor(M, N, device=device)
         self.dyqt = NVFP4Tensor(N, M, device=device)
+        self.scratch = torch.empty(LINEAR_SCRATCH_BYTES, dtype=torch.uint8, device=device)
         self.cctx = c_linear_ctx(M, K, N, self.xq.c(), self.wq.c(), self.wqt.c(), self.xqt.c(),
-                                 self.dyq.c(), self.dyqt.c())
+                                 self.dyq.c(), self.dyqt.c(), 0, 0,
+                                 ctypes.c_void_p(self.scratch.data_ptr()), LINEAR_SCRATCH_BYTES)
 
     @classmethod
     def from_buffer(cls, M: int, K: int, N: int, device="cuda"):

@@ -322,6 +322,7 @@ nvfp4_status nvfp4_linear_ctx_bytes(int64_t M, int64_t K, int64_t N, size_t* byt
     total += align256((size_t)(rc[i][0] * (rc[i][1] / 16)));  // 1x16-sized scales
     total += 256;                                              // tensor scale
   }
+  total += NVFP4_LINEAR_SCRATCH_BYTES;                          // backward split scratch
   *bytes = total;
   return NVFP4_OK;
 }
@@ -353,6 +354,8 @@ nvfp4_status nvfp4_linear_ctx_init(nvfp4_linear_ctx* ctx, void* buffer, size_t b
   ctx->N = N;
   ctx->rht_signs = 0;
   ctx->rht = 0;
+  ctx->wgrad_scratch = p;
+  ctx->wgrad_scratch_bytes = NVFP4_LINEAR_SCRATCH_BYTES;
   return NVFP4_OK;
 }
 
@@ -732,7 +735,8 @@ nvfp4_status nvfp4_linear_bwd(const void* dy, int32_t dtype, nvfp4_linear_ctx* c
   // (one launch: the Wgrad tiles fill the Dgrad tail)
   NVFP4_HIP(launch_gemm_pair(gemm_operand(&ctx->dyq), gemm_operand(&ctx->wqt), N, dx, kDtypeBF16,
                              K, gemm_operand(&ctx->dyqt), gemm_operand(&ctx->xqt), M, dw,
-                             dw_dtype == NVFP4_BF16 ? kDtypeBF16 : kDtypeF32, K, s));
+                             dw_dtype == NVFP4_BF16 ? kDtypeBF16 : kDtypeF32, K,
+                             static_cast<float*>(ctx->wgrad_scratch), ctx->wgrad_scratch_bytes, s));
   return NVFP4_OK;
 }
 

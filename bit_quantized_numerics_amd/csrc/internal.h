@@ -77,10 +77,13 @@ hipError_t launch_mx_gemm(const GemmOperand& a, const GemmOperand& b, int64_t K,
 hipError_t launch_bf16_gemm(const void* a, int64_t M, const void* b, int64_t N, int64_t K, void* c,
                             int c_dtype, int64_t ldc, hipStream_t s);
 // Two independent GEMMs in one launch where the kernel allows it (so that the
-// tail of one fills with the tiles of the other), else two launches.
+// tail of one fills with the tiles of the other), else two launches.  With
+// `scratch` (>= split_scratch_bytes(), 16-byte aligned) the second GEMM's last
+// tiles may run as two K halves added by a combine pass (shorter last round).
 hipError_t launch_gemm_pair(const GemmOperand& a0, const GemmOperand& b0, int64_t K0, void* c0,
                             int c0_dtype, int64_t ldc0, const GemmOperand& a1,
                             const GemmOperand& b1, int64_t K1, void* c1, int c1_dtype,
-                            int64_t ldc1, hipStream_t s);
+                            int64_t ldc1, float* scratch, size_t scratch_bytes, hipStream_t s);
+size_t split_scratch_bytes();
 
 }  // namespace nvfp4

@@ -164,7 +164,20 @@ typedef struct {
    * would get another transform than X^T (dW = (R dY)^T (R X) needs one R). */
   uint32_t rht_signs;
   int32_t rht;
+  /* Optional fp32 scratch for the backward's fused Dgrad + Wgrad launch
+   * (device memory, 16-byte aligned, NVFP4_LINEAR_SCRATCH_BYTES): with it the
+   * last Wgrad tiles of each XCD's share run as two K halves and a short pass
+   * adds the halves, which evens out the launch's last round.  The halves are
+   * summed in another order than a whole tile's K loop, so dW may differ from
+   * nvfp4_gemm's in the last bits (within the GEMM tolerance); NULL keeps
+   * every tile whole.  nvfp4_linear_ctx_init places it in its buffer. */
+  void* wgrad_scratch;
+  size_t wgrad_scratch_bytes;
 } nvfp4_linear_ctx;
+
+/* Size of nvfp4_linear_ctx.wgrad_scratch: 8 XCD shares x 8 split tiles x 2
+ * halves x 256 x 256 fp32. */
+#define NVFP4_LINEAR_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* ------------------------------------------------------------ size queries */
 

@@ -208,12 +208,14 @@ def test_bf16_gemm_and_switch_argument_errors():
 def test_linear_ctx_bytes_and_init():
     with pytest.raises(nv.NVFP4Error):
         nv.nvfp4_linear_ctx_bytes(1 << 40, 1 << 30, 16)   # sizes past 2^62 bytes
-    """One-buffer layout of the six layer operands (host bookkeeping only)."""
+    """One-buffer layout of the six layer operands and the backward's split
+    scratch (host bookkeeping only)."""
     M, K, N = 64, 96, 160
     nbytes = nv.nvfp4_linear_ctx_bytes(M, K, N)
     a256 = lambda v: (v + 255) // 256 * 256
     shapes = [(M, K), (N, K), (K, N), (K, M), (M, N), (N, M)]
-    assert nbytes == sum(a256(r * c // 2) + a256(r * c // 16) + 256 for r, c in shapes)
+    assert nbytes == sum(a256(r * c // 2) + a256(r * c // 16) + 256
+                         for r, c in shapes) + nv.LINEAR_SCRATCH_BYTES
     base = 1 << 24
     ctx = nv.c_linear_ctx()
     assert nv._lib.nvfp4_linear_ctx_init(ctypes.byref(ctx), base, nbytes, M, K, N) == nv.OK
@@ -226,7 +228,8 @@ def test_linear_ctx_bytes_and_init():
         assert t.scales == t.codes + a256(r * c // 2)
         assert t.global_scale == t.scales + a256(r * c // 16)
         end = t.global_scale + 256
-    assert end == base + nbytes
+    assert ctx.wgrad_scratch == end and ctx.wgrad_scratch_bytes == nv.LINEAR_SCRATCH_BYTES
+    assert end + nv.LINEAR_SCRATCH_BYTES == base + nbytes
     assert (ctx.wq.scale_mode, ctx.xq.scale_mode) == (nv.SCALE_16X16, nv.SCALE_1X16)
     f = nv._lib.nvfp4_linear_ctx_init
     assert f(ctypes.byref(ctx), base, nbytes - 1, M, K, N) == nv.ERR_SHAPE
