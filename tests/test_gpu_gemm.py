@@ -191,3 +191,23 @@ def test_mfma_loop_ceiling(nv):
     assert 500.0 < pure < 2600.0, pure
     fp4 = nv.nvfp4_peak_mfma_fp4(500)
     assert 1000.0 < fp4 < 10200.0, fp4
+
+
+def test_tensor_scale_rewritten_between_launches(nv, ws):
+    """The GEMM reads g_A and g_B at kernel entry: re-quantising A in place
+    with another tensor amax (x 64) between two launches must change the
+    product accordingly (no stale value from an earlier launch)."""
+    M, N, K = 512, 512, 1024
+    a = np32(_rand(M, K, 41))
+    b = np32(_rand(N, K, 42, scale=0.02))
+    say("gemm tensor scale rewritten")
+    qa = nv.nvfp4_quantize(torch.from_numpy(a).cuda(), ws)
+    qb = nv.nvfp4_quantize(torch.from_numpy(b).cuda(), ws)
+    rb = O.quantize(b)
+    for k, scale in enumerate((1.0, 64.0, 1.0 / 8)):
+        ak = a * np.float32(scale)
+        nv.nvfp4_quantize(torch.from_numpy(ak).cuda(), ws, out=qa)
+        ra = O.quantize(ak)
+        C, S = O.gemm(ra, rb)
+        c = nv.nvfp4_gemm(qa, qb, torch.float32)
+        assert_gemm_close(c.cpu().numpy(), C, S, False, f"call {k} (A x {scale})")
