@@ -323,12 +323,18 @@ hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int
 
 // ---------------------------------------------------------------- emit
 
-// Reads one copy's amax word; flags the status word and returns false when
-// the amax is not finite (that copy is then skipped).
-__device__ __forceinline__ bool copy_scales(const uint32_t* amax, uint32_t* status,
-                                            TensorScales* ts, uint32_t* amax_bits = nullptr) {
+// The lane's tensor-amax slot of one copy (lanes past the slots read 0).
+__device__ __forceinline__ uint32_t amax_slot(const uint32_t* amax) {
   const int lane = threadIdx.x & 63;
-  const uint32_t bits = wave_max_u32(lane < kAmaxSlots ? amax[lane * kAmaxStride] : 0u);
+  return lane < kAmaxSlots ? amax[lane * kAmaxStride] : 0u;
+}
+
+// The copy's tensor scales from the wave's slot values (amax_slot); flags the
+// status word and returns false when the amax is not finite (that copy is
+// then skipped).
+__device__ __forceinline__ bool copy_scales(uint32_t slot, uint32_t* status, TensorScales* ts,
+                                            uint32_t* amax_bits = nullptr) {
+  const uint32_t bits = wave_max_u32(slot);
   if (amax_bits) *amax_bits = bits;
   if (bits >= kInfBits) {
     if (threadIdx.x == 0) atomicMax(status, kStatusNonfinite);
@@ -478,13 +484,22 @@ void quant_tile_kernel(TileArgs a) {
   TensorScales tr{}, tc{};
   bool do_row = false, do_col = false;
   uint32_t col_amax = 0;
-  if (ROW) do_row = copy_scales(a.row.amax, a.status, &tr);
+  // the amax slots first, then the tile's data: the data loads (independent
+  // of the scales) are in flight while the slots are reduced and the
+  // multiplier tables filled
+  constexpr bool kColSlots = COL && !(TWO_D && ROW);
+  const uint32_t slot_row = ROW ? amax_slot(a.row.amax) : 0u;
+  const uint32_t slot_col = kColSlots ? amax_slot(a.col.amax) : 0u;
+  RawPatch<TIn> p;
+  load_raw(static_cast<const TIn*>(a.x), tile_r0, min(rows - tile_r0, (int64_t)TR), cols, a.ld,
+           rs * 16, c0, p);
+  if (ROW) do_row = copy_scales(slot_row, a.status, &tr);
   if (COL) {
     if (TWO_D && ROW) {
       do_col = do_row;
       tc = tr;
     } else {
-      do_col = copy_scales(a.col.amax, a.status, &tc, &col_amax);
+      do_col = copy_scales(slot_col, a.status, &tc, &col_amax);
     }
   }
   // Folding the transform's final 1/4 (1/2 for d = 4) into the multiplier.
@@ -512,9 +527,6 @@ void quant_tile_kernel(TileArgs a) {
   }
   __syncthreads();
 
-  RawPatch<TIn> p;
-  load_raw(static_cast<const TIn*>(a.x), tile_r0, min(rows - tile_r0, (int64_t)TR), cols, a.ld,
-           rs * 16, c0, p);
 
   if (TWO_D) {
     // ---- one scale per 16x16 tile [Review s2]: this patch and lane ^ 1's
