@@ -50,10 +50,10 @@ BYTES_2D_RUN = BYTES_2D + 2.0
 # HBM traffic of the GEMM kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (KiB per dispatch; FETCH_SIZE x 2 and WRITE_SIZE x 1, the factors a plain
 # 1 GiB device copy reads back), averaged over the single Fprop, Dgrad and
-# Wgrad launches: 1031.1, 861.9 and 1252.6 MB.  Valid only for the kernel
+# Wgrad launches: 999.4, 790.3 and 1243.9 MB.  Valid only for the kernel
 # source it was measured on (profiles/hbm_traffic_gemm_quantize_*.md).
-GEMM_TRAFFIC = {"source_sha1": "fcf9d1a74252a0600f9fae0c2b397efcc0f98a74",
-                "bytes_per_launch": 1048.5e6}
+GEMM_TRAFFIC = {"source_sha1": "ed02f68775c7e418de31a51cf6e8325fdab15199",
+                "bytes_per_launch": 1011.2e6}
 
 
 def _gemm_source_sha1() -> str:

@@ -75,7 +75,7 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kGemmThreads = 256;
-constexpr int kGroupM = 8;  // tile-row group for L2 reuse
+constexpr int kGroupM = 4;  // tile-row group for L2 reuse
 
 // ------------------------------------------------------------ inner loop
 
